@@ -1,0 +1,322 @@
+"""activation_fp8_quant_amd -- fused activation FP8 quantisation for MI355X.
+
+Thin Python binding over ``libafq.so`` (C ABI in ``include/afq.h``): it
+allocates output tensors with PyTorch, marshals pointers and the current HIP
+stream into the ABI descriptors, and raises on a non-zero status.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+
+Entry points (same names as the C ABI):
+    fused_add_rmsnorm_quant(x, weight, eps, ...)   residual add + RMSNorm + quant
+    silu_mul_quant(gate_up, mode, ...)             SiLU-and-mul + quant
+    fp8_quant(x, mode, ...)                        standalone row-wise quant
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence, Union
+
+import torch  # loaded first: the library then binds to torch's HIP runtime
+
+__all__ = [
+    "MXFP8", "BLOCK128", "PER_TOKEN", "STANDARD", "GEMMA",
+    "QuantizedActivation", "AfqError",
+    "fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant",
+    "abi_version", "status_string", "library_path", "load",
+]
+
+# ---------------------------------------------------------------- constants
+MXFP8, BLOCK128, PER_TOKEN = 0, 1, 2
+STANDARD, GEMMA = 0, 1
+_BF16, _FP16, _FP32 = 0, 1, 2
+_DTYPE_TAG = {torch.bfloat16: _BF16, torch.float16: _FP16, torch.float32: _FP32}
+_MODE_NAMES = {"mxfp8": MXFP8, "mx": MXFP8, "block128": BLOCK128, "b128": BLOCK128,
+               "per_token": PER_TOKEN, "pt": PER_TOKEN}
+_KIND_NAMES = {"standard": STANDARD, "gemma": GEMMA}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libafq.so")
+
+
+class AfqError(RuntimeError):
+    """A non-zero status returned by libafq."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+# ------------------------------------------------------------ ABI structs
+class _QAct(ctypes.Structure):
+    _fields_ = [("values", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("normed", ctypes.c_void_p)]
+
+
+class _NormSeg(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_row_stride", ctypes.c_int64),
+                ("weight", ctypes.c_void_p), ("cols", ctypes.c_int64), ("out", _QAct)]
+
+
+class _NormDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("nseg", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("residual_in", ctypes.c_void_p),
+                ("residual_out", ctypes.c_void_p), ("seg", _NormSeg * 2)]
+
+
+class _ActDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("I", ctypes.c_int64), ("gate_up", ctypes.c_void_p),
+                ("gate_up_row_stride", ctypes.c_int64), ("mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("out", _QAct)]
+
+
+class _QuantDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("cols", ctypes.c_int64), ("x", ctypes.c_void_p),
+                ("x_row_stride", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("out", _QAct)]
+
+
+_lib = None
+
+
+def load():
+    """Load libafq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m activation_fp8_quant_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(library_path)
+    for name, desc in (("fused_add_rmsnorm_quant", _NormDesc), ("silu_mul_quant", _ActDesc),
+                       ("fp8_quant", _QuantDesc)):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(desc), ctypes.c_void_p]
+    lib.afq_status_string.restype = ctypes.c_char_p
+    lib.afq_status_string.argtypes = [ctypes.c_int]
+    lib.afq_abi_version.restype = ctypes.c_int
+    lib.afq_abi_version.argtypes = []
+    lib.afq_last_hip_error.restype = ctypes.c_int
+    lib.afq_last_hip_error.argtypes = []
+    _check_single_hip_runtime()
+    _lib = lib
+    return lib
+
+
+def _check_single_hip_runtime():
+    """The library must share torch's HIP runtime (one libamdhip64 mapped),
+    otherwise torch's streams and pointers mean nothing to it."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise ImportError(f"two HIP runtimes are mapped: {sorted(real)}")
+
+
+def abi_version() -> int:
+    return load().afq_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load().afq_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------- results
+@dataclasses.dataclass
+class QuantizedActivation:
+    """Codes and scales of a quantised activation (the tuple a quantised
+    linear consumes), with the optional rounded activation and residual.
+
+    values   float8_e4m3fn [M, cols]
+    scales   MXFP8: uint8 E8M0 bytes [M, cols/32]; BLOCK128: float32
+             [M, cols/128]; PER_TOKEN: float32 [M, 1]
+    normed   the rounded activation in its dtype, or None
+    residual the updated residual h = x + r (norm with residual), or None
+    """
+    values: torch.Tensor
+    scales: torch.Tensor
+    normed: Optional[torch.Tensor]
+    residual: Optional[torch.Tensor]
+    mode: int
+    orig_dtype: torch.dtype
+    orig_shape: tuple
+
+
+def _mode(m) -> int:
+    if isinstance(m, str):
+        return _MODE_NAMES[m.lower()]
+    if m not in (MXFP8, BLOCK128, PER_TOKEN):
+        raise ValueError(f"unknown quant mode {m!r}")
+    return int(m)
+
+
+def _kind(k) -> int:
+    if isinstance(k, str):
+        return _KIND_NAMES[k.lower()]
+    if k not in (STANDARD, GEMMA):
+        raise ValueError(f"unknown norm kind {k!r}")
+    return int(k)
+
+
+def _scales_shape(mode: int, M: int, cols: int):
+    if mode == MXFP8:
+        return (M, cols // 32), torch.uint8
+    if mode == BLOCK128:
+        return (M, cols // 128), torch.float32
+    return (M, 1), torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _rowmajor(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _alloc_out(mode, M, cols, device, normed_dtype, out):
+    if out is not None:
+        return out
+    sshape, sdtype = _scales_shape(mode, M, cols)
+    values = torch.empty((M, cols), dtype=torch.float8_e4m3fn, device=device)
+    scales = torch.empty(sshape, dtype=sdtype, device=device)
+    normed = torch.empty((M, cols), dtype=normed_dtype, device=device) if normed_dtype else None
+    return values, scales, normed
+
+
+# ------------------------------------------------------------- entry points
+def fused_add_rmsnorm_quant(
+    x: Union[torch.Tensor, Sequence[torch.Tensor]],
+    weight: Union[torch.Tensor, Sequence[torch.Tensor]],
+    eps: float,
+    *,
+    mode=MXFP8,
+    kind=GEMMA,
+    residual: Optional[torch.Tensor] = None,
+    residual_out: Optional[torch.Tensor] = None,
+    inplace: bool = False,
+    want_normed: bool = False,
+    out=None,
+    stream=None,
+):
+    """Residual add + RMSNorm + FP8 quantisation in one launch.
+
+    x / weight   one [M, cols] tensor and its [cols] weight, or two of each
+                 (two independent row segments, e.g. the q and kv inputs of
+                 MLA attention, normed in one launch with separate weights)
+    residual     [M, cols] or None.  The updated residual h = x + residual
+                 goes to residual_out (a new tensor by default, `residual`
+                 itself with inplace=True).
+    want_normed  also return the normed rows rounded to the input dtype.
+    out          optional preallocated (values, scales, normed) per segment
+                 (a tuple, or a list of tuples for two segments).
+    Returns a QuantizedActivation, or a list of two for two segments.
+    """
+    lib = load()
+    mode, kind = _mode(mode), _kind(kind)
+    xs = [x] if isinstance(x, torch.Tensor) else list(x)
+    ws = [weight] if isinstance(weight, torch.Tensor) else list(weight)
+    if len(xs) != len(ws) or len(xs) not in (1, 2):
+        raise ValueError("x and weight must both be one tensor or two tensors")
+    outs = [out] if (out is None or len(xs) == 1) else list(out)
+    if len(outs) == 1 and len(xs) == 2:
+        outs = [None, None]
+    dtype = xs[0].dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("norm inputs must be bfloat16 or float16")
+    M = xs[0].shape[0]
+    d = _NormDesc()
+    d.M, d.nseg, d.kind, d.dtype, d.mode = M, len(xs), kind, _DTYPE_TAG[dtype], mode
+    d.eps = float(eps)
+    results = []
+    for i, (xi, wi) in enumerate(zip(xs, ws)):
+        _rowmajor(xi, "x")
+        if xi.dtype != dtype or wi.dtype != dtype or xi.shape[0] != M:
+            raise ValueError("segments must share dtype and row count")
+        if wi.dim() != 1 or wi.shape[0] != xi.shape[1] or not wi.is_contiguous():
+            raise ValueError("weight must be a contiguous [cols] tensor")
+        cols = xi.shape[1]
+        values, scales, normed = _alloc_out(mode, M, cols, xi.device,
+                                            dtype if want_normed else None, outs[i])
+        seg = d.seg[i]
+        seg.x, seg.x_row_stride, seg.weight, seg.cols = xi.data_ptr(), xi.stride(0), wi.data_ptr(), cols
+        seg.out.values, seg.out.scales, seg.out.normed = _ptr(values), _ptr(scales), _ptr(normed)
+        results.append(QuantizedActivation(values, scales, normed, None, mode, dtype, tuple(xi.shape)))
+    if residual is not None:
+        if len(xs) != 1:
+            raise ValueError("a residual is only supported with one segment")
+        _rowmajor(residual, "residual")
+        if not residual.is_contiguous() or residual.dtype != dtype or residual.shape != xs[0].shape:
+            raise ValueError("residual must be a contiguous tensor shaped and typed like x")
+        if residual_out is None:
+            residual_out = residual if inplace else torch.empty_like(residual)
+        d.residual_in, d.residual_out = residual.data_ptr(), residual_out.data_ptr()
+        results[0].residual = residual_out
+    st = lib.fused_add_rmsnorm_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    if st != 0:
+        raise AfqError(st, "fused_add_rmsnorm_quant")
+    return results[0] if len(results) == 1 else results
+
+
+def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
+                   out=None, stream=None) -> QuantizedActivation:
+    """SiLU-and-mul of a bf16 [M, 2I] row ([gate | up]) + FP8 quantisation.
+
+    MXFP8 quantises the fp32 activation; BLOCK128 rounds silu and the product
+    to bf16 first (the unfused SiluAndMul).  want_act also returns the bf16
+    activation.
+    """
+    lib = load()
+    mode = _mode(mode)
+    _rowmajor(gate_up, "gate_up")
+    if gate_up.dtype != torch.bfloat16:
+        raise TypeError("gate_up must be bfloat16")
+    M, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    I = two_i // 2
+    values, scales, act = _alloc_out(mode, M, I, gate_up.device,
+                                     torch.bfloat16 if want_act else None, out)
+    d = _ActDesc()
+    d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
+    d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
+    st = lib.silu_mul_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    if st != 0:
+        raise AfqError(st, "silu_mul_quant")
+    return QuantizedActivation(values, scales, act, None, mode, gate_up.dtype, (M, I))
+
+
+def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> QuantizedActivation:
+    """Standalone row-wise FP8 quantisation of a bf16 / fp16 / fp32 [M, cols]."""
+    lib = load()
+    mode = _mode(mode)
+    _rowmajor(x, "x")
+    if x.dtype not in _DTYPE_TAG:
+        raise TypeError("x must be bfloat16, float16 or float32")
+    M, cols = x.shape
+    values, scales, _ = _alloc_out(mode, M, cols, x.device, None, out)
+    d = _QuantDesc()
+    d.M, d.cols, d.x, d.x_row_stride = M, cols, x.data_ptr(), x.stride(0)
+    d.dtype, d.mode = _DTYPE_TAG[x.dtype], mode
+    d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), None
+    st = lib.fp8_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    if st != 0:
+        raise AfqError(st, "fp8_quant")
+    return QuantizedActivation(values, scales, None, None, mode, x.dtype, (M, cols))

@@ -1,0 +1,132 @@
+"""Pins of the oracle's (residual add +) RMSNorm + quantisation:
+exact brute force on tiny rows, closed forms and invariants."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from activation_fp8_quant_amd import inputs
+from tests import brute
+from tests._compare import ord8, ord16
+
+MODES = {"mx": orc.MXFP8, "b128": orc.BLOCK128, "pt": orc.PER_TOKEN}
+KINDS = {"gemma": orc.GEMMA, "standard": orc.STANDARD}
+DTYPES = {"bf16": orc.BF16, "fp16": orc.FP16}
+
+
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+@pytest.mark.parametrize("kind", ["gemma", "standard"])
+@pytest.mark.parametrize("dtype,H", [("bf16", 128), ("fp16", 128), ("bf16", 256)])
+def test_norm_quant_matches_exact_brute_force(mode, kind, dtype, H):
+    M = 3
+    d = inputs.norm_inputs(M, H, seed=11, x_std=3.0, r_std=1.0,
+                           w_kind="normal" if kind == "gemma" else "uniform",
+                           w_param=0.1 if kind == "gemma" else 0.5, dtype=dtype)
+    out = orc.norm_quant(d["x"], d["w"], residual=d["r"], kind=KINDS[kind],
+                         dtype=DTYPES[dtype], mode=MODES[mode], eps=1e-6)
+    for i in range(M):
+        ref = brute.norm_row(d["x"][i], d["r"][i], d["w"], kind, dtype, mode, 1e-6)
+        assert list(out["h"][i]) == ref["h"]
+        assert list(out["normed"][i]) == ref["normed"]
+        assert np.array_equal(ord8(out["values"][i]), ord8(np.array(ref["codes"], np.uint8)))
+        if mode == "mx":
+            assert list(out["scales"][i]) == ref["scales"]
+        else:
+            assert np.array_equal(out["scales"][i].view(np.uint32),
+                                  np.array(ref["scales"], np.float32).view(np.uint32))
+
+
+def test_norm_without_residual_matches_brute_force():
+    d = inputs.norm_inputs(2, 128, seed=12, x_std=1.0, r_std=None, w_kind="uniform", w_param=0.5)
+    out = orc.norm_quant(d["x"], d["w"], residual=None, kind=orc.STANDARD, dtype=orc.BF16,
+                         mode=orc.PER_TOKEN, eps=1e-6)
+    assert out["h"] is None
+    for i in range(2):
+        ref = brute.norm_row(d["x"][i], None, d["w"], "standard", "bf16", "pt", 1e-6)
+        assert list(out["normed"][i]) == ref["normed"]
+        assert np.array_equal(ord8(out["values"][i]), ord8(np.array(ref["codes"], np.uint8)))
+
+
+def _f(bits, dtype="bf16"):
+    return inputs.bits_to_float(bits, dtype).astype(np.float64)
+
+
+def test_constant_row_closed_form():
+    """h = c everywhere: y = c * g / sqrt(c^2 + eps)."""
+    H, c, eps = 256, 0.75, 1e-6
+    x = inputs.to_bits(np.full((1, H), c))
+    w = inputs.to_bits(np.linspace(-0.5, 0.5, H))
+    out = orc.norm_quant(x, w, kind=orc.GEMMA, dtype=orc.BF16, mode=orc.MXFP8, eps=eps)
+    g = 1.0 + _f(w)
+    y = c * g / np.sqrt(c * c + np.float64(np.float32(eps)))
+    assert np.array_equal(out["normed"][0], orc.round_bf16(y))
+
+
+def test_all_zero_row():
+    for mode in (orc.MXFP8, orc.BLOCK128, orc.PER_TOKEN):
+        x = np.zeros((2, 256), np.uint16)
+        w = inputs.to_bits(np.ones(256))
+        out = orc.norm_quant(x, w, kind=orc.STANDARD, dtype=orc.BF16, mode=mode, eps=1e-6)
+        assert not (out["values"] & 0x7F).any()
+        assert not out["scales"].astype(np.float64).any()
+
+
+@pytest.mark.parametrize("mode", [orc.MXFP8, orc.BLOCK128, orc.PER_TOKEN])
+def test_scale_invariance_eps0(mode):
+    """RMSNorm is invariant to scaling its input by 2^k when eps = 0."""
+    d = inputs.norm_inputs(4, 512, seed=13, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    xa, ra = _f(d["x"]), _f(d["r"])
+    ref = orc.norm_quant(d["x"], d["w"], residual=d["r"], kind=orc.STANDARD, dtype=orc.BF16,
+                         mode=mode, eps=0.0)
+    for k in (-20, 7):
+        x2, r2 = inputs.to_bits(xa * 2.0 ** k), inputs.to_bits(ra * 2.0 ** k)
+        out = orc.norm_quant(x2, d["w"], residual=r2, kind=orc.STANDARD, dtype=orc.BF16,
+                             mode=mode, eps=0.0)
+        assert np.array_equal(out["normed"], ref["normed"])
+        assert np.array_equal(out["values"], ref["values"])
+        assert np.array_equal(out["scales"], ref["scales"])
+
+
+def test_gemma_zero_weight_unit_rms():
+    """w = 0 (Gemma g = 1), eps = 0: mean(y^2) = 1 up to the bf16 rounding."""
+    d = inputs.norm_inputs(8, 2048, seed=14, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    w = np.zeros(2048, np.uint16)
+    out = orc.norm_quant(d["x"], w, residual=d["r"], kind=orc.GEMMA, dtype=orc.BF16,
+                         mode=orc.MXFP8, eps=0.0)
+    y = _f(out["normed"])
+    ms = (y * y).mean(axis=1)
+    assert np.all(np.abs(ms - 1.0) < 2.0 ** -7)
+
+
+def test_residual_add_is_torch_bf16_add():
+    """h equals PyTorch's bf16 addition (fp32 add, one rounding)."""
+    import torch
+    d = inputs.norm_inputs(16, 1024, seed=15, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    out = orc.norm_quant(d["x"], d["w"], residual=d["r"], kind=orc.GEMMA, dtype=orc.BF16,
+                         mode=orc.MXFP8, eps=1e-6)
+    tx = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16)
+    tr = torch.from_numpy(d["r"].view(np.int16)).view(torch.bfloat16)
+    ref = (tx + tr).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out["h"], ref)
+
+
+def test_weight_kind_differs():
+    """Gemma uses (1 + w), standard w: with w = 0 the standard norm gives 0."""
+    d = inputs.norm_inputs(2, 256, seed=16, x_std=1.0, r_std=None, w_kind="normal", w_param=0.1)
+    w = np.zeros(256, np.uint16)
+    s = orc.norm_quant(d["x"], w, kind=orc.STANDARD, dtype=orc.BF16, mode=orc.MXFP8, eps=1e-6)
+    g = orc.norm_quant(d["x"], w, kind=orc.GEMMA, dtype=orc.BF16, mode=orc.MXFP8, eps=1e-6)
+    assert not (ord16(s["normed"])).any()
+    assert (ord16(g["normed"]) != 0).mean() > 0.99
+
+
+def test_edge_rows_brute_force():
+    H = 128
+    rows = inputs.edge_rows(H)
+    x = inputs.to_bits(rows)
+    w = inputs.to_bits(np.random.default_rng(3).uniform(0.5, 1.5, H))
+    for mode in ("mx", "b128", "pt"):
+        out = orc.norm_quant(x, w, kind=orc.STANDARD, dtype=orc.BF16, mode=MODES[mode], eps=1e-6)
+        for i in range(rows.shape[0]):
+            ref = brute.norm_row(x[i], None, w, "standard", "bf16", mode, 1e-6)
+            assert list(out["normed"][i]) == ref["normed"], (mode, i)
+            assert np.array_equal(ord8(out["values"][i]), ord8(np.array(ref["codes"], np.uint8))), (mode, i)
