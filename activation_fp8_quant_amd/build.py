@@ -1,0 +1,51 @@
+"""Build libafq.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+    python -m activation_fp8_quant_amd.build
+
+The library is placed next to this file so that it travels with the source
+tree.  Always recompiles (a build check must compile).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libafq.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are kept out of the generated code.
+NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    kobj = os.path.join(BUILD, "afq_kernels.o")
+    aobj = os.path.join(BUILD, "afq_abi.o")
+    _run([HIPCC, "-c", f"--offload-arch={ARCH}", *COMMON, *NO_PACKED_FP32,
+          "-x", "hip", os.path.join(CSRC, "afq_kernels.hip"), "-o", kobj])
+    # the ABI translation unit is plain host C++ (no HIP headers)
+    _run(["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+          f"-I{INCLUDE}", f"-I{CSRC}", os.path.join(CSRC, "afq_abi.cpp"), "-o", aobj])
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,364 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle,
+element by element on seeded inputs shaped like the pages' workloads, at
+sizes spanning several tiles and a ragged tail, plus edge rows."""
+import numpy as np
+import pytest
+import torch
+
+import activation_fp8_quant_amd as afq
+import oracle as orc
+from activation_fp8_quant_amd import inputs
+from tests._compare import check_codes, check_dtype16, check_scales, scales_u8_or_f32
+from tests._gpu import (MODE, ORC_DT, check_norm, dev16, host8, host16, ref_norm, run_norm)
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, stats):
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+# ------------------------------------------------------------ norm paths
+@pytest.mark.parametrize("M", [8, 67])
+def test_norm_gemma_mx_h6144(M):
+    """Fused add + Gemma RMSNorm + MXFP8 + bf16 copy at the decode shape
+    (hidden 6144): x ~ N(0,3^2), r ~ N(0,1), w ~ N(0,0.1^2), eps 1e-6."""
+    d = inputs.norm_inputs(M, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    _report(f"gemma-mx M={M}", check_norm(gpu, ref, "mx", "bf16", "gemma-mx"))
+
+
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+@pytest.mark.parametrize("kind", ["gemma", "standard"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("H,M", [(4096, 33), (2048, 5), (1024, 130), (512, 9)])
+def test_norm_modes(mode, kind, dtype, H, M):
+    d = inputs.norm_inputs(M, H, seed=3, x_std=1.0, r_std=1.0,
+                           w_kind="uniform" if kind == "standard" else "normal",
+                           w_param=0.5 if kind == "standard" else 0.1, dtype=dtype)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind=kind, mode=mode, dtype=dtype)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind=kind, mode=mode, dtype=dtype)
+    _report(f"{mode}-{kind}-{dtype} H={H} M={M}", check_norm(gpu, ref, mode, dtype, "norm"))
+
+
+@pytest.mark.parametrize("H", [2176, 12288, 32768, 128, 8])
+def test_norm_widths(H):
+    mode = "b128" if H % 128 == 0 else "pt"
+    d = inputs.norm_inputs(7, H, seed=4, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="standard", mode=mode)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode=mode)
+    _report(f"width {H} {mode}", check_norm(gpu, ref, mode, "bf16", f"width{H}"))
+    if H % 32 == 0:
+        gpu = run_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="mx")
+        ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="mx")
+        check_norm(gpu, ref, "mx", "bf16", f"width{H}-mx")
+
+
+def test_norm_without_residual_and_without_copy():
+    d = inputs.norm_inputs(20, 4096, seed=5, x_std=1.0, r_std=None, w_kind="uniform", w_param=0.5)
+    for mode in ("mx", "b128", "pt"):
+        gpu = run_norm(d["x"], d["w"], kind="standard", mode=mode, want_normed=False)
+        ref = ref_norm(d["x"], d["w"], kind="standard", mode=mode)
+        check_codes(gpu["values"], ref["values"], mode)
+        check_scales(gpu["scales"], ref["scales"], MODE[mode], mode)
+
+
+def test_norm_inplace_residual():
+    d = inputs.norm_inputs(16, 6144, seed=6, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    xt, wt, rt = dev16(d["x"]), dev16(d["w"]), dev16(d["r"])
+    qa = afq.fused_add_rmsnorm_quant(xt, wt, 1e-6, mode=afq.MXFP8, kind=afq.GEMMA, residual=rt,
+                                     inplace=True, want_normed=True)
+    torch.cuda.synchronize()
+    assert qa.residual.data_ptr() == rt.data_ptr()
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    check_dtype16(host16(rt), ref["h"], "inplace h", exact=True)
+
+
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+def test_norm_edge_rows(mode):
+    H = 2048
+    rows = inputs.edge_rows(H)
+    x = inputs.to_bits(rows)
+    r = inputs.to_bits(np.zeros_like(rows))
+    w = inputs.to_bits(np.random.default_rng(3).uniform(0.5, 1.5, H))
+    for kind in ("standard", "gemma"):
+        gpu = run_norm(x, w, r=r, kind=kind, mode=mode)
+        ref = ref_norm(x, w, r=r, kind=kind, mode=mode)
+        _report(f"edge {mode} {kind}", check_norm(gpu, ref, mode, "bf16", f"edge-{mode}-{kind}"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M", [1, 8, 64, 1024])
+def test_two_segment_per_token(dtype, M):
+    """q [M,1536] and kv [M,512] normed in one launch with separate weights,
+    per-token scales each; inputs with 1 % x50 outliers; q and kv are column
+    slices of one [M, 2112] buffer (the fused qkv_a projection output)."""
+    segs = inputs.two_segment_inputs(M, (1536, 512), seed=0, dtype=dtype)
+    buf = np.zeros((M, 2112), np.uint16)
+    buf[:, :1536] = segs[0]["x"]
+    buf[:, 1536:2048] = segs[1]["x"]
+    bt = dev16(buf, dtype)
+    xq, xkv = bt[:, :1536], bt[:, 1536:2048]
+    wq, wkv = dev16(segs[0]["w"], dtype), dev16(segs[1]["w"], dtype)
+    outs = afq.fused_add_rmsnorm_quant([xq, xkv], [wq, wkv], 1e-6, mode=afq.PER_TOKEN,
+                                       kind=afq.STANDARD, want_normed=True)
+    torch.cuda.synchronize()
+    for s, qa in zip(segs, outs):
+        assert qa.orig_dtype == (torch.bfloat16 if dtype == "bf16" else torch.float16)
+        gpu = dict(normed=host16(qa.normed), values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
+        ref = ref_norm(s["x"], s["w"], kind="standard", mode="pt", dtype=dtype)
+        _report(f"two-seg {dtype} M={M} cols={s['x'].shape[1]}", check_norm(gpu, ref, "pt", dtype, "two-seg"))
+
+
+def test_two_segment_other_modes():
+    segs = inputs.two_segment_inputs(12, (1536, 512), seed=2)
+    for mode in ("mx", "b128"):
+        xs = [dev16(s["x"]) for s in segs]
+        ws = [dev16(s["w"]) for s in segs]
+        outs = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=MODE[mode], kind=afq.STANDARD,
+                                           want_normed=True)
+        torch.cuda.synchronize()
+        for s, qa in zip(segs, outs):
+            gpu = dict(normed=host16(qa.normed), values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
+            ref = ref_norm(s["x"], s["w"], kind="standard", mode=mode)
+            check_norm(gpu, ref, mode, "bf16", f"two-seg-{mode}")
+
+
+# ----------------------------------------------------------- SiLU-and-mul
+def _run_silu(gu, mode):
+    qa = afq.silu_mul_quant(dev16(gu), MODE[mode], want_act=True)
+    torch.cuda.synchronize()
+    return dict(values=host8(qa.values), scales=scales_u8_or_f32(qa.scales), act=host16(qa.normed))
+
+
+@pytest.mark.parametrize("M", [8, 16, 192, 300])
+def test_silu_mx_i768(M):
+    gu = inputs.gate_up_inputs(M, 768, seed=0, std=2.0)
+    gpu = _run_silu(gu, "mx")
+    ref = orc.silu_quant(gu, orc.MXFP8, threads=8)
+    n1 = check_codes(gpu["values"], ref["values"], "silu-mx")
+    nb = check_scales(gpu["scales"], ref["scales"], 0, "silu-mx")
+    na = check_dtype16(gpu["act"], ref["act"], "silu-mx act")
+    _report(f"silu-mx M={M}", dict(codes_1=n1, scales_bad=nb, act_1ulp=na))
+
+
+@pytest.mark.parametrize("I,M", [(12288, 1), (12288, 32), (3072, 64), (2176, 9), (1536, 33)])
+def test_silu_b128(I, M):
+    gu = inputs.gate_up_inputs(M, I, seed=1, std=1.0)
+    gpu = _run_silu(gu, "b128")
+    ref = orc.silu_quant(gu, orc.BLOCK128, threads=8)
+    # the bf16 activation of this mode is computed exactly: bit-identical
+    check_dtype16(gpu["act"], ref["act"], "silu-b128 act", exact=True)
+    assert np.array_equal(gpu["values"], ref["values"])
+    assert np.array_equal(gpu["scales"].view(np.uint32), ref["scales"].view(np.uint32))
+
+
+def test_silu_b128_all_gates_exact():
+    """bf16(silu(g)) for every finite bf16 gate (up = 1): bit-identical."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    gates = c[((c >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    pad = (-gates.size) % 128
+    g = np.concatenate([gates, np.zeros(pad, np.uint16)]).reshape(-1, 128)
+    one = inputs.to_bits(np.ones(1))[0]
+    gu = np.concatenate([g, np.full_like(g, one)], axis=1)
+    gpu = _run_silu(gu, "b128")
+    ref = orc.silu_quant(gu, orc.BLOCK128, threads=8)
+    bad = np.flatnonzero(gpu["act"].ravel() != ref["act"].ravel())
+    assert bad.size == 0, [hex(int(gu.reshape(-1, 256)[i // 128, i % 128])) for i in bad[:10]]
+    assert np.array_equal(gpu["values"], ref["values"])
+
+
+def test_silu_mx_extreme_gates():
+    rng = np.random.default_rng(9)
+    g = rng.standard_normal((4, 256)) * 30.0
+    g[0, :64] = -rng.uniform(80, 100, 64)     # e^-g beyond the fp32 range
+    g[1, :] = rng.uniform(-95, -85, 256)       # whole blocks of tiny activations
+    u = rng.standard_normal((4, 256)) * 2.0
+    gu = np.concatenate([inputs.to_bits(g), inputs.to_bits(u)], axis=1)
+    gpu = _run_silu(gu, "mx")
+    ref = orc.silu_quant(gu, orc.MXFP8)
+    check_codes(gpu["values"], ref["values"], "silu-mx-extreme")
+    check_scales(gpu["scales"], ref["scales"], 0, "silu-mx-extreme")
+
+
+# --------------------------------------------------------- standalone quant
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+def test_fp8_quant_standalone(dtype, mode):
+    rng = np.random.default_rng(10)
+    M, n = 37, 3072
+    x = rng.standard_normal((M, n)) * 2.0 ** rng.integers(-12, 12, (M, 1))
+    x[0] = 0.0
+    x[1, ::5] *= 1000.0
+    if dtype == "fp32":
+        xh = x.astype(np.float32)
+        xt = torch.from_numpy(xh).cuda()
+        odt = orc.FP32
+    else:
+        xh = inputs.to_bits(x, dtype)
+        xt = dev16(xh, dtype)
+        odt = ORC_DT[dtype]
+    qa = afq.fp8_quant(xt, MODE[mode])
+    torch.cuda.synchronize()
+    q, s = orc.quant(xh, odt, MODE[mode], threads=8)
+    assert np.array_equal(host8(qa.values), q)
+    gs = scales_u8_or_f32(qa.scales)
+    if mode == "mx":
+        assert np.array_equal(gs, s)
+    else:
+        assert np.array_equal(gs.view(np.uint32), s.view(np.uint32))
+
+
+def test_e4m3_conversion_structured_fp32():
+    """Every fp32 exponent that reaches e4m3 (codes 0..448), all 2^5 top
+    mantissa patterns times boundary low bits, both signs: quantised with
+    unit scale (each 32-block holds a 256.0 anchor, so the E8M0 byte is
+    127) and compared code by code with the oracle."""
+    exps = np.arange(0, 136, dtype=np.uint32)          # up to 2^8 binade
+    top = np.arange(32, dtype=np.uint32) << 18
+    low = np.array([0, 1, 2, 0x1FFFF, 0x20000, 0x20001, 0x3FFFF, 0x10000, 0x30000], dtype=np.uint32)
+    bits = (exps[:, None, None] << 23) | top[None, :, None] | low[None, None, :]
+    bits = bits.ravel()
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    vals = bits.view(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    per = 31
+    nblk = (vals.size + per - 1) // per
+    buf = np.zeros((nblk, 32), np.float32)
+    flat = np.zeros(nblk * per, np.float32)
+    flat[:vals.size] = vals
+    buf[:, 1:] = flat.reshape(nblk, per)
+    buf[:, 0] = 256.0
+    cols = 32 * 64
+    pad = (-nblk) % 64
+    buf = np.concatenate([buf, np.zeros((pad, 32), np.float32)]).reshape(-1, cols)
+    qa = afq.fp8_quant(torch.from_numpy(buf).cuda(), afq.MXFP8)
+    torch.cuda.synchronize()
+    q, s = orc.quant(buf, orc.FP32, orc.MXFP8, threads=8)
+    got = host8(qa.values)
+    bad = np.flatnonzero(got.ravel() != q.ravel())
+    assert bad.size == 0, [(float(buf.ravel()[i]), hex(got.ravel()[i]), hex(q.ravel()[i])) for i in bad[:8]]
+
+
+def test_fp32_quotient_exact_bf16_all_values():
+    """1x128 codes of every positive bf16 mantissa against group maxima of
+    every mantissa: e4m3(fp32(u/s)) must match the oracle exactly."""
+    rng = np.random.default_rng(11)
+    mant = np.arange(128)
+    rows = []
+    for am in range(128):
+        A = (1 + am / 128.0) * 2.0 ** int(rng.integers(-20, 20))
+        # 127 values in [0, A] drawn from all mantissas / nearby exponents, then the max
+        e = np.floor(np.log2(A))
+        v = (1 + rng.permutation(mant)[:127] / 128.0) * 2.0 ** (e - rng.integers(0, 12, 127))
+        v = np.minimum(v, A) * np.where(rng.random(127) < 0.5, -1, 1)
+        rows.append(np.concatenate([[A], v]))
+    x = inputs.to_bits(np.array(rows))
+    qa = afq.fp8_quant(dev16(x), afq.BLOCK128)
+    torch.cuda.synchronize()
+    q, s = orc.quant(x, orc.BF16, orc.BLOCK128)
+    assert np.array_equal(host8(qa.values), q)
+
+
+# ------------------------------------------------------ execution properties
+def test_deterministic_and_batch_invariant():
+    d = inputs.norm_inputs(67, 6144, seed=12, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    a = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    b = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    for k in ("h", "normed", "values", "scales"):
+        assert np.array_equal(a[k], b[k]), k
+    c = run_norm(d["x"][5:13], d["w"], r=d["r"][5:13], kind="gemma", mode="mx")
+    for k in ("h", "normed", "values", "scales"):
+        assert np.array_equal(a[k][5:13], c[k]), k
+
+
+def test_graph_replay_equals_eager():
+    d = inputs.norm_inputs(32, 6144, seed=13, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    xt, wt, rt = dev16(d["x"]), dev16(d["w"]), dev16(d["r"])
+    eager = afq.fused_add_rmsnorm_quant(xt, wt, 1e-6, mode=afq.MXFP8, kind=afq.GEMMA, residual=rt,
+                                        want_normed=True)
+    gu = dev16(inputs.gate_up_inputs(32, 768, seed=13, std=2.0))
+    eager_s = afq.silu_mul_quant(gu, afq.MXFP8)
+    torch.cuda.synchronize()
+    outs = (torch.empty_like(eager.values), torch.empty_like(eager.scales), torch.empty_like(eager.normed))
+    res_out = torch.empty_like(rt)
+    souts = (torch.empty_like(eager_s.values), torch.empty_like(eager_s.scales), None)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            afq.fused_add_rmsnorm_quant(xt, wt, 1e-6, mode=afq.MXFP8, kind=afq.GEMMA, residual=rt,
+                                        residual_out=res_out, want_normed=True, out=outs)
+            afq.silu_mul_quant(gu, afq.MXFP8, out=souts)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in (*outs, res_out, souts[0], souts[1]):
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.uint8), eager.values.view(torch.uint8)), rep
+        assert torch.equal(outs[1], eager.scales), rep
+        assert torch.equal(outs[2], eager.normed), rep
+        assert torch.equal(res_out, eager.residual), rep
+        assert torch.equal(souts[0].view(torch.uint8), eager_s.values.view(torch.uint8)), rep
+        assert torch.equal(souts[1], eager_s.scales), rep
+
+
+def test_guard_bands_untouched():
+    """Outputs carved from larger poisoned buffers: bytes outside each output
+    stay untouched, bytes inside are all written."""
+    M, H = 9, 2048
+    d = inputs.norm_inputs(M, H, seed=14, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    for mode in ("mx", "b128", "pt"):
+        sshape = {"mx": (M, H // 32), "b128": (M, H // 128), "pt": (M, 1)}[mode]
+        sbytes = int(np.prod(sshape)) * (1 if mode == "mx" else 4)
+        guard = 256
+        vb = torch.full((M * H + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        sb = torch.full((sbytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        nb = torch.full((M * H * 2 + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        values = vb[guard:guard + M * H].view(torch.float8_e4m3fn).view(M, H)
+        scales = sb[guard:guard + sbytes]
+        scales = scales.view(sshape) if mode == "mx" else scales.view(torch.float32).view(sshape)
+        normed = nb[guard:guard + 2 * M * H].view(torch.bfloat16).view(M, H)
+        afq.fused_add_rmsnorm_quant(dev16(d["x"]), dev16(d["w"]), 1e-6, mode=MODE[mode],
+                                    kind=afq.STANDARD, residual=dev16(d["r"]),
+                                    out=(values, scales, normed))
+        torch.cuda.synchronize()
+        for buf in (vb, sb, nb):
+            assert bool((buf[:guard] == 0x5A).all()) and bool((buf[-guard:] == 0x5A).all()), mode
+        ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode=mode)
+        check_codes(host8(values), ref["values"], mode)
+        check_scales(scales_u8_or_f32(scales), ref["scales"], MODE[mode], mode)
+        check_dtype16(host16(normed), ref["normed"], mode)
+
+
+def test_rejected_call_writes_nothing():
+    M, H = 4, 256
+    x = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    values = torch.full((M, H), 7, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    scales = torch.full((M, H // 32), 9, dtype=torch.uint8, device="cuda")
+    with pytest.raises(afq.AfqError) as e:
+        # scales overlapping the codes: an alias error, detected on the host
+        afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=afq.MXFP8, out=(values, values.view(torch.uint8)[:, :8], None))
+    assert e.value.status == -5
+    torch.cuda.synchronize()
+    assert bool((values.view(torch.uint8) == 7).all())
+
+
+# ------------------------------------------------------- full-size sampled
+def test_full_size_prefill_sampled_rows():
+    """The benchmark workload (M = 16384, H = 6144, seed 1, x, r ~ N(0,3^2)),
+    launched exactly as timed; 96 sampled rows checked against the oracle."""
+    M, H = 16384, 6144
+    d = inputs.norm_inputs(M, H, seed=1, x_std=3.0, r_std=3.0, w_kind="normal", w_param=0.1)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx")
+    rows = np.sort(np.random.default_rng(0).choice(M, 96, replace=False))
+    rows[-1] = M - 1
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode="mx", rows=rows)
+    sub = {k: (None if v is None else v[rows]) for k, v in gpu.items()}
+    rsub = {k: (None if v is None else v[rows]) for k, v in ref.items()}
+    _report("full-size sampled", check_norm(sub, rsub, "mx", "bf16", "full"))
