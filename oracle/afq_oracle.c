@@ -361,6 +361,11 @@ int orc_norm_quant_rows(int64_t M, int64_t H, const void *x, int64_t x_stride,
  */
 static void silu_2(double g, double *hi, double *lo)
 {
+    if (g == 0.0) { /* g * logistic(g) keeps the sign of a zero gate */
+        *hi = g;
+        *lo = 0.0;
+        return;
+    }
     if (fabs(g) < 0.5) {
         double a = g / 2.0, b = (g / 2.0) * tanh(g / 2.0);
         double s = a + b;           /* |a| >= |b|: the error of s is exact */
