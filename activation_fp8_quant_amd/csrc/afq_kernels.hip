@@ -22,12 +22,10 @@
 namespace afq {
 
 // ===================================================================== norm
-template <int NT>
-struct RowShape {
-    static constexpr int BS = NT < 256 ? 256 : NT;   // threads per block
-    static constexpr int R = BS / NT;                // rows per block
-    static constexpr int WPR = NT / 64;              // wavefronts per row
-};
+// Rows are NT lanes (a whole number of wavefronts, NT <= 1024); a block
+// holds R rows.  Both are launch parameters; the per-lane chunk count CPL
+// is a template parameter (the loops over a lane's chunks are unrolled).
+constexpr int kMaxBlock = 1024;
 
 struct NormArgs {
     NormSegPlan seg[2];
@@ -36,23 +34,29 @@ struct NormArgs {
     int64_t M;
     float eps;
     int32_t nseg;
-    int32_t gemma;
     int32_t C0;      // chunks of segment 0
     int32_t C;       // chunks of both segments
+    int32_t NT;      // lanes per row
+    int32_t R;       // rows per block
+    int32_t WPR;     // wavefronts per row
 };
 
-template <int DT, int MODE, int NT, int CPL>
-__global__ void __launch_bounds__(RowShape<NT>::BS)
+template <int DT, int MODE, bool GEMMA, int CPL>
+__global__ void __launch_bounds__(kMaxBlock)
 norm_quant_kernel(const NormArgs a)
 {
-    using S = RowShape<NT>;
-    static_assert(NT >= 64 && NT % 64 == 0, "rows are whole wavefronts");
     const int tid = threadIdx.x;
-    const int rib = tid / NT;
-    const int t = tid % NT;
-    const int64_t row = (int64_t)blockIdx.x * S::R + rib;
+    const int wave = tid >> 6;
+    const int rib = wave / a.WPR;            // row within the block
+    const int t = tid - rib * a.NT;          // lane within the row
+    const int64_t row = (int64_t)blockIdx.x * a.R + rib;
     const bool row_ok = row < a.M;
     const bool has_res = a.res_in != nullptr;
+
+    // per-row bases: x of each segment, the residual rows, and the output
+    // rows (codes, scales, copy) of each segment
+    const uint8_t *xrow[2] = {a.seg[0].x + row * a.seg[0].x_pitch, a.seg[1].x + row * a.seg[1].x_pitch};
+    const int64_t rrow = row * a.C0 * 16;
 
     // ---- issue every load of the row
     uint4 xv[CPL], rv[CPL], wv[CPL];
@@ -60,37 +64,31 @@ norm_quant_kernel(const NormArgs a)
     int sg[CPL], lc[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
-        const int c = t + k * NT;
+        const int c = t + k * a.NT;
         ok[k] = row_ok && c < a.C;
         sg[k] = c >= a.C0 ? 1 : 0;
         lc[k] = c - (sg[k] ? a.C0 : 0);
         if (ok[k]) {
-            const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
-            xv[k] = ldg<uint4>(s.x + row * s.x_pitch + (int64_t)lc[k] * 16);
-            wv[k] = ldg<uint4>(s.w + (int64_t)lc[k] * 16);
+            xv[k] = ldg<uint4>((sg[k] ? xrow[1] : xrow[0]) + lc[k] * 16);
+            wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
             if (has_res)
-                rv[k] = ldg<uint4>(a.res_in + (row * a.C0 + lc[k]) * 16);
+                rv[k] = ldg<uint4>(a.res_in + rrow + lc[k] * 16);
         }
     }
 
-    // ---- residual add, sum of squares
+    // ---- residual add (h = round_dt(x + r), stored), sum of squares
     float h[CPL][8];
     float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
-        float xf[8];
-        unpack8<DT>(xv[k], xf);
+        unpack8<DT>(xv[k], h[k]);
         if (has_res) {
-            float rf[8], sum[8];
+            float rf[8];
             unpack8<DT>(rv[k], rf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sum[i] = xf[i] + rf[i];
-            const uint4 hp = round_pack8<DT>(sum, h[k]);
-            stg<uint4>(a.res_out + (row * a.C0 + lc[k]) * 16, hp);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[k][i] = xf[i];
+            for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
+            stg<uint4>(a.res_out + rrow + lc[k] * 16, round8<DT>(h[k]));
         }
         float p = 0.f;
 #pragma unroll
@@ -99,70 +97,61 @@ norm_quant_kernel(const NormArgs a)
     }
 
     // ---- row reduction: DPP inside the wavefront, LDS across wavefronts
-    ss0 = sum_lanes<64>(ss0);
-    if (a.nseg > 1) ss1 = sum_lanes<64>(ss1);
-    if constexpr (S::WPR > 1) {
-        __shared__ float red[S::R][S::WPR][2];
-        const int w = t / 64;
-        if ((t & 63) == 0) {
-            red[rib][w][0] = ss0;
-            red[rib][w][1] = ss1;
+    __shared__ float red[kMaxBlock / 64][2];
+    __shared__ float redm[kMaxBlock / 64][2];
+    ss0 = sum_wave(ss0);
+    if (a.nseg > 1) ss1 = sum_wave(ss1);
+    if (a.WPR > 1) {
+        if ((tid & 63) == 0) {
+            red[wave][0] = ss0;
+            red[wave][1] = ss1;
         }
         __syncthreads();
         ss0 = 0.f;
         ss1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < S::WPR; ++i) {
-            ss0 += red[rib][i][0];
-            ss1 += red[rib][i][1];
+        for (int i = 0; i < a.WPR; ++i) {
+            ss0 += red[rib * a.WPR + i][0];
+            ss1 += red[rib * a.WPR + i][1];
         }
     }
     const float inv0 = 1.0f / __builtin_sqrtf(ss0 / (float)a.seg[0].cols + a.eps);
     const float inv1 = a.nseg > 1 ? 1.0f / __builtin_sqrtf(ss1 / (float)a.seg[1].cols + a.eps) : 0.f;
 
-    // ---- y = h * inv * g, rounded to the dtype (u, kept in place of h),
-    //      optional copy
-    float (&u)[CPL][8] = h;
-    uint32_t am0 = 0, am1 = 0;
+    // ---- u = round_dt(h * inv * g), kept in place of h; optional copy
+    float am0 = 0.f, am1 = 0.f;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
         const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
         const float inv = sg[k] ? inv1 : inv0;
-        float wf[8], y[8];
+        float wf[8];
         unpack8<DT>(wv[k], wf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float g = a.gemma ? 1.0f + wf[i] : wf[i];
-            y[i] = (h[k][i] * inv) * g;
-        }
-        const uint4 up = round_pack8<DT>(y, u[k]);
+        for (int i = 0; i < 8; ++i) h[k][i] = (h[k][i] * inv) * (GEMMA ? 1.0f + wf[i] : wf[i]);
+        const uint4 up = round8<DT>(h[k]);
         if (s.normed)
             stg<uint4>(s.normed + (row * s.cols + (int64_t)lc[k] * 8) * 2, up);
         if constexpr (MODE == kPT) {
-            const uint32_t m = amax_bits8(u[k]);
-            if (sg[k]) am1 = max(am1, m); else am0 = max(am0, m);
+            const float m = amax8(h[k]);
+            if (sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
         }
     }
 
     // ---- quantise
     if constexpr (MODE == kPT) {
-        am0 = max_lanes<64>(am0);
-        if (a.nseg > 1) am1 = max_lanes<64>(am1);
-        if constexpr (S::WPR > 1) {
-            __shared__ uint32_t redm[S::R][S::WPR][2];
-            const int w = t / 64;
-            if ((t & 63) == 0) {
-                redm[rib][w][0] = am0;
-                redm[rib][w][1] = am1;
+        am0 = max_wave(am0);
+        if (a.nseg > 1) am1 = max_wave(am1);
+        if (a.WPR > 1) {
+            if ((tid & 63) == 0) {
+                redm[wave][0] = am0;
+                redm[wave][1] = am1;
             }
             __syncthreads();
-            am0 = 0;
-            am1 = 0;
-#pragma unroll
-            for (int i = 0; i < S::WPR; ++i) {
-                am0 = max(am0, redm[rib][i][0]);
-                am1 = max(am1, redm[rib][i][1]);
+            am0 = 0.f;
+            am1 = 0.f;
+            for (int i = 0; i < a.WPR; ++i) {
+                am0 = __builtin_fmaxf(am0, redm[rib * a.WPR + i][0]);
+                am1 = __builtin_fmaxf(am1, redm[rib * a.WPR + i][1]);
             }
         }
         const Fp32Scale sc0 = fp32_scale(am0);
@@ -171,7 +160,7 @@ norm_quant_kernel(const NormArgs a)
         for (int k = 0; k < CPL; ++k) {
             if (!ok[k]) continue;
             const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
-            const uint2 q = fp32scale_codes8(u[k], sg[k] ? sc1 : sc0);
+            const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
             stg<uint2>(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
             if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
         }
@@ -182,14 +171,12 @@ norm_quant_kernel(const NormArgs a)
             const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
             uint2 q;
             if constexpr (MODE == kMX) {
-                const uint32_t am = max_quad(amax_bits8(u[k]));
-                const uint32_t b = e8m0_from_amax_bits(am);
-                q = mx_codes8(u[k], mx_inv_scale(b));
+                const uint32_t b = e8m0_of(max_quad(amax8(h[k])));
+                q = mx_codes8(h[k], mx_inv_scale(b));
                 if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b;
             } else {
-                const uint32_t am = max_row16(amax_bits8(u[k]));
-                const Fp32Scale sc = fp32_scale(am);
-                q = fp32scale_codes8(u[k], sc);
+                const Fp32Scale sc = fp32_scale(max_row16(amax8(h[k])));
+                q = fp32scale_codes8(h[k], sc);
                 if ((lc[k] & 15) == 0)
                     reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
             }
@@ -211,7 +198,7 @@ struct ActArgs {
     double invC;      // 1 / C, for the row index of a flat chunk
 };
 
-// Row of flat chunk f: a float estimate corrected by at most one step.
+// Row of flat chunk f: an fp64 estimate corrected by at most one step.
 __device__ __forceinline__ int64_t row_of(int64_t f, int32_t C, double invC)
 {
     int64_t r = (int64_t)((double)f * invC);
@@ -220,41 +207,108 @@ __device__ __forceinline__ int64_t row_of(int64_t f, int32_t C, double invC)
     return r;
 }
 
-// silu(g) in fp32, within a few ulp for g >= -80 (exp and an IEEE
-// division); below that e^-g leaves the fp32 range and the value is
-// computed in fp64 instead.
-__device__ __forceinline__ float silu_f32(float g)
+// silu(g) = g / (1 + e^-g) in fp32 for g >= -80, within a few ulp:
+// e^-g = 2^t with t = -g log2(e) carried as hi + lo (the product's exact
+// rounding error by FMA plus the tail of log2(e)), 2^t = exp2(hi) (1 + lo
+// ln2) with the hardware exp2, then g times the hardware reciprocal.  For
+// g > 80, e^-g < 2^-115 vanishes next to 1 either way, so the exponent is
+// taken at min(g, 80) (keeps -g log2(e) finite for the largest gates).
+__device__ __forceinline__ float silu_fast(float g)
 {
-    if (g < -80.0f) {
-        const double gd = (double)g;
-        return (float)(gd / (1.0 + exp(-gd)));
-    }
-    return g / (1.0f + expf(-g));
+    constexpr float kL2eHi = 1.44269502162933349609375f;   // RN(log2 e)
+    constexpr float kL2eLo = 1.925963033500011e-08f;       // log2 e - kL2eHi
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float gc = __builtin_fminf(g, 80.0f);
+    const float t = -gc * kL2eHi;
+    const float tl = __builtin_fmaf(-gc, kL2eHi, -t) + (-gc) * kL2eLo;
+    const float e0 = __builtin_amdgcn_exp2f(t);
+    const float e = __builtin_fmaf(e0, tl * kLn2, e0);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// bf16(silu(g)) for a bf16 gate, exactly rounded: the fp32 value is
-// accurate to a few ulp, so its bf16 rounding is the exact one unless the
-// value sits within 16 fp32 ulps of a bf16 rounding midpoint (or e^-g
-// leaves the fp32 range); those rare cases are redone in fp64.
-__device__ __forceinline__ uint32_t silu_bf16(float g)
+// silu in fp64 as a two-term value hi + lo: for |g| < 1/2 as g/2 + (g/2)
+// tanh(g/2) (for tiny g the plain quotient collapses to exactly g/2, a
+// possible rounding midpoint, and the second term keeps the g^2/4 that
+// decides it); else g e^g / (1 + e^g) (g < 0, no overflow) or
+// g / (1 + e^-g).  A zero gate returns itself (silu(-0) = -0).
+__device__ __forceinline__ void silu_f64(float g, double &hi, double &lo)
 {
-    const float s = g / (1.0f + expf(-g));
-    const uint32_t low = __float_as_uint(s) & 0xFFFFu;
-    if (g < -80.0f || (low >= 0x8000u - 16u && low <= 0x8000u + 16u)) {
-        const double gd = (double)g;
-        const double sd = gd / (1.0 + exp(-gd));
-        const uint32_t sign = sd < 0.0 ? 0x8000u : 0u;
-        const double ad = __builtin_fabs(sd);
-        if (ad < 0x1p-126) // bf16 subnormals: a count of 2^-133 steps, RNE
-            return sign | (uint32_t)__builtin_rint(ad * 0x1p133);
-        // fp64 keeps 52 mantissa bits, bf16 7: drop 45 with RNE (a carry
-        // moves into the exponent field by itself)
-        const uint64_t db = (uint64_t)__double_as_longlong(ad);
-        const uint64_t rn = db + ((1ull << 44) - 1) + ((db >> 45) & 1ull);
-        const uint32_t e8 = (uint32_t)((rn >> 52) - 1023 + 127);
-        return sign | (e8 << 7) | (uint32_t)((rn >> 45) & 0x7Full);
+    const double gd = (double)g;
+    lo = 0.0;
+    if (gd == 0.0) {
+        hi = gd;
+    } else if (__builtin_fabs(gd) < 0.5) {
+        const double a = gd * 0.5, b = a * tanh(a);
+        hi = a + b;
+        lo = b - (hi - a);
+    } else if (gd < 0.0) {
+        const double e = exp(gd);
+        hi = gd * e / (1.0 + e);
+    } else {
+        hi = gd / (1.0 + exp(-gd));
     }
-    return f32_to_bf16(s);
+}
+
+__device__ __noinline__ float silu_f32_slow(float g)
+{
+    double hi, lo;
+    silu_f64(g, hi, lo);
+    return (float)(hi + lo);
+}
+
+// fp32 silu for the MXFP8 path: the fast form, or fp64 where e^-g leaves
+// the fp32 range.
+__device__ __forceinline__ float silu_f32(float g)
+{
+    return g < -80.0f ? silu_f32_slow(g) : silu_fast(g);
+}
+
+// bf16 code of the two-term value hi + lo (lo a correction far below an
+// fp64 ulp of hi that only decides an exact midpoint of hi), sign given
+// separately; round to nearest even.
+__device__ __forceinline__ uint32_t bf16_of_double2(double hi, double lo, uint32_t sign)
+{
+    const double ad = __builtin_fabs(hi);
+    const double t = hi < 0.0 ? -lo : lo; // the tail, measured along |hi|
+    if (ad < 0x1p-126) {
+        // bf16 subnormals: a count of 2^-133 steps
+        const double k = ad * 0x1p133; // exact scaling
+        const double kf = __builtin_floor(k);
+        const double fr = k - kf;       // exact
+        uint32_t c = (uint32_t)kf;
+        if (fr > 0.5 || (fr == 0.5 && (t > 0.0 || (t == 0.0 && (c & 1u))))) ++c;
+        return sign | c;
+    }
+    // fp64 keeps 52 mantissa bits, bf16 7: drop 45 (a carry of the round-up
+    // moves into the exponent field), then rebias the exponent 1023 -> 127
+    const uint64_t db = (uint64_t)__double_as_longlong(ad);
+    const uint64_t rem = db & ((1ull << 45) - 1);
+    uint64_t base = db >> 45;
+    const uint64_t half = 1ull << 44;
+    if (rem > half || (rem == half && (t > 0.0 || (t == 0.0 && (base & 1ull))))) ++base;
+    return sign | (uint32_t)(base - ((uint64_t)(1023 - 127) << 7));
+}
+
+__device__ __noinline__ uint32_t silu_bf16_slow(float g)
+{
+    double hi, lo;
+    silu_f64(g, hi, lo);
+    // silu(g) = g * logistic(g) has the sign of g (also for -0 and for
+    // underflow to zero)
+    return bf16_of_double2(hi, lo, (__float_as_uint(g) >> 16) & 0x8000u);
+}
+
+// bf16(silu(g)) for a bf16 gate, exactly rounded.  The fast fp32 value is
+// within a few ulp, so its bf16 rounding is the exact one unless it sits
+// within 16 fp32 ulps of a bf16 rounding midpoint, or e^-g leaves the fp32
+// range; those rare cases are redone in fp64.
+__device__ __forceinline__ float silu_bf16(float g)
+{
+    const float s = silu_fast(g);
+    const uint32_t low = __float_as_uint(s) & 0xFFFFu;
+    if (g < -80.0f || (low - (0x8000u - 16u)) <= 32u)
+        return __uint_as_float(silu_bf16_slow(g) << 16);
+    return bf16_lo(f32_to_bf16(s));
 }
 
 template <int MODE, int CPL>
@@ -281,30 +335,24 @@ act_quant_kernel(const ActArgs a)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue; // uniform over every quant group
-        float g[8], up[8], v[8];
+        float g[8], v[8];
         unpack8<kBF16>(gv[k], g);
-        unpack8<kBF16>(uv[k], up);
+        unpack8<kBF16>(uv[k], v);
         const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
         uint2 q;
         if constexpr (MODE == kMX) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = silu_f32(g[i]) * up[i];
-            if (a.act) {
-                float dummy[8];
-                stg<uint4>(a.act + out_off * 2, round_pack8<kBF16>(v, dummy));
-            }
-            const uint32_t am = max_quad(amax_bits8(v));
-            const uint32_t b = e8m0_from_amax_bits(am);
+            for (int i = 0; i < 8; ++i) v[i] *= silu_f32(g[i]);
+            if (a.act) stg<uint4>(a.act + out_off * 2, pack8<kBF16>(v));
+            const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
         } else {
-            float sgm[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sgm[i] = __uint_as_float(silu_bf16(g[i]) << 16) * up[i];
-            const uint4 ap = round_pack8<kBF16>(sgm, v);
+            for (int i = 0; i < 8; ++i) v[i] *= silu_bf16(g[i]);
+            const uint4 ap = round8<kBF16>(v);
             if (a.act) stg<uint4>(a.act + out_off * 2, ap);
-            const uint32_t am = max_row16(amax_bits8(v));
-            const Fp32Scale sc = fp32_scale(am);
+            const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
             q = fp32scale_codes8(v, sc);
             if ((lc[k] & 15) == 0)
                 reinterpret_cast<float *>(a.scales)[rw[k] * (a.I / 128) + lc[k] / 16] = sc.s;
@@ -324,6 +372,9 @@ struct QuantArgs {
     int32_t C;       // chunks per row
     int32_t cols;
     double invC;
+    int32_t NT;      // lanes per row (row kernel)
+    int32_t R;       // rows per block (row kernel)
+    int32_t WPR;     // wavefronts per row (row kernel)
 };
 
 template <int DT>
@@ -364,11 +415,11 @@ quant_flat_kernel(const QuantArgs a)
         const int64_t out_off = rw[k] * a.cols + (int64_t)lc[k] * 8;
         uint2 q;
         if constexpr (MODE == kMX) {
-            const uint32_t b = e8m0_from_amax_bits(max_quad(amax_bits8(v[k])));
+            const uint32_t b = e8m0_of(max_quad(amax8(v[k])));
             q = mx_codes8(v[k], mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.cols / 32) + lc[k] / 4] = (uint8_t)b;
         } else {
-            const Fp32Scale sc = fp32_scale(max_row16(amax_bits8(v[k])));
+            const Fp32Scale sc = fp32_scale(max_row16(amax8(v[k])));
             q = fp32scale_codes8(v[k], sc);
             if ((lc[k] & 15) == 0)
                 reinterpret_cast<float *>(a.scales)[rw[k] * (a.cols / 128) + lc[k] / 16] = sc.s;
@@ -377,99 +428,106 @@ quant_flat_kernel(const QuantArgs a)
     }
 }
 
-template <int DT, int NT, int CPL>
-__global__ void __launch_bounds__(RowShape<NT>::BS)
+template <int DT, int CPL>
+__global__ void __launch_bounds__(kMaxBlock)
 quant_row_kernel(const QuantArgs a)
 {
-    using S = RowShape<NT>;
     constexpr int EB = DT == kFP32 ? 4 : 2;
     const int tid = threadIdx.x;
-    const int rib = tid / NT;
-    const int t = tid % NT;
-    const int64_t row = (int64_t)blockIdx.x * S::R + rib;
+    const int wave = tid >> 6;
+    const int rib = wave / a.WPR;
+    const int t = tid - rib * a.NT;
+    const int64_t row = (int64_t)blockIdx.x * a.R + rib;
     const bool row_ok = row < a.M;
     float v[CPL][8];
     bool ok[CPL];
-    uint32_t am = 0;
+    float am = 0.f;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
-        const int c = t + k * NT;
+        const int c = t + k * a.NT;
         ok[k] = row_ok && c < a.C;
         if (ok[k]) load_chunk<DT>(a.x + row * a.x_pitch + (int64_t)c * 8 * EB, v[k]);
     }
 #pragma unroll
     for (int k = 0; k < CPL; ++k)
-        if (ok[k]) am = max(am, amax_bits8(v[k]));
-    am = max_lanes<64>(am);
-    if constexpr (S::WPR > 1) {
-        __shared__ uint32_t redm[S::R][S::WPR];
-        if ((t & 63) == 0) redm[rib][t / 64] = am;
+        if (ok[k]) am = __builtin_fmaxf(am, amax8(v[k]));
+    am = max_wave(am);
+    __shared__ float redm[kMaxBlock / 64];
+    if (a.WPR > 1) {
+        if ((tid & 63) == 0) redm[wave] = am;
         __syncthreads();
-        am = 0;
-#pragma unroll
-        for (int i = 0; i < S::WPR; ++i) am = max(am, redm[rib][i]);
+        am = 0.f;
+        for (int i = 0; i < a.WPR; ++i) am = __builtin_fmaxf(am, redm[rib * a.WPR + i]);
     }
     const Fp32Scale sc = fp32_scale(am);
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
-        const int c = t + k * NT;
+        const int c = t + k * a.NT;
         stg<uint2>(a.values + row * a.cols + (int64_t)c * 8, fp32scale_codes8(v[k], sc));
         if (c == 0) reinterpret_cast<float *>(a.scales)[row] = sc.s;
     }
 }
 
 // ================================================================ launchers
-// Threads per row and chunks per lane for a row of C chunks: the smallest
-// whole number of wavefronts (power of two, 64..1024) that covers the row
-// with at most 4 chunks per lane.
-static void row_config(int C, int &NT, int &CPL)
+// Row shape for a row of C chunks.  Few rows (latency-bound: every lane of
+// a row works through its chunks one after the other, so the row's time
+// grows with the chunks per lane): as many lanes as chunks, up to 1024.
+// Many rows (bandwidth-bound): about 256 lanes per row, at most 4 chunks
+// per lane.  NT is a whole number of wavefronts; rows of fewer than 256
+// lanes are packed several to a block.
+struct RowShapeRt {
+    int NT, CPL, R, WPR;
+};
+static RowShapeRt row_shape(int C, int64_t M)
 {
-    NT = 64;
-    while (NT < 1024 && NT * 4 < C) NT *= 2;
-    CPL = (C + NT - 1) / NT;
+    RowShapeRt s;
+    const bool few_rows = M <= 1024;
+    int cpl = few_rows ? (C + 1023) / 1024 : (C + 255) / 256;
+    cpl = cpl < 1 ? 1 : (cpl > 4 ? 4 : cpl);
+    if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
+    int nt = (C + cpl - 1) / cpl;
+    nt = (nt + 63) / 64 * 64;
+    s.NT = nt;
+    s.CPL = (C + nt - 1) / nt;
+    s.R = (nt < 256 && 256 % nt == 0) ? 256 / nt : 1;
+    s.WPR = nt / 64;
+    return s;
 }
 
-template <int DT, int MODE, int NT, int CPL>
+template <int DT, int MODE, bool GEMMA, int CPL>
 static hipError_t go_norm(const NormArgs &a, hipStream_t st)
 {
-    using S = RowShape<NT>;
-    const int64_t blocks = (a.M + S::R - 1) / S::R;
-    hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, NT, CPL>), dim3((unsigned)blocks),
-                       dim3(S::BS), 0, st, a);
+    const int64_t blocks = (a.M + a.R - 1) / a.R;
+    hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL>), dim3((unsigned)blocks),
+                       dim3(a.NT * a.R), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, int MODE, int NT>
+template <int DT, int MODE, bool GEMMA>
 static hipError_t go_norm_cpl(const NormArgs &a, int CPL, hipStream_t st)
 {
     switch (CPL) {
-    case 1: return go_norm<DT, MODE, NT, 1>(a, st);
-    case 2: return go_norm<DT, MODE, NT, 2>(a, st);
-    case 3: return go_norm<DT, MODE, NT, 3>(a, st);
-    default: return go_norm<DT, MODE, NT, 4>(a, st);
+    case 1: return go_norm<DT, MODE, GEMMA, 1>(a, st);
+    case 2: return go_norm<DT, MODE, GEMMA, 2>(a, st);
+    case 3: return go_norm<DT, MODE, GEMMA, 3>(a, st);
+    default: return go_norm<DT, MODE, GEMMA, 4>(a, st);
     }
 }
 
 template <int DT, int MODE>
-static hipError_t go_norm_nt(const NormArgs &a, int NT, int CPL, hipStream_t st)
+static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int CPL, hipStream_t st)
 {
-    switch (NT) {
-    case 64: return go_norm_cpl<DT, MODE, 64>(a, CPL, st);
-    case 128: return go_norm_cpl<DT, MODE, 128>(a, CPL, st);
-    case 256: return go_norm_cpl<DT, MODE, 256>(a, CPL, st);
-    case 512: return go_norm_cpl<DT, MODE, 512>(a, CPL, st);
-    default: return go_norm_cpl<DT, MODE, 1024>(a, CPL, st);
-    }
+    return gemma ? go_norm_cpl<DT, MODE, true>(a, CPL, st) : go_norm_cpl<DT, MODE, false>(a, CPL, st);
 }
 
 template <int DT>
-static hipError_t go_norm_mode(const NormArgs &a, int mode, int NT, int CPL, hipStream_t st)
+static hipError_t go_norm_mode(const NormArgs &a, int mode, bool gemma, int CPL, hipStream_t st)
 {
     switch (mode) {
-    case kMX: return go_norm_nt<DT, kMX>(a, NT, CPL, st);
-    case kB128: return go_norm_nt<DT, kB128>(a, NT, CPL, st);
-    default: return go_norm_nt<DT, kPT>(a, NT, CPL, st);
+    case kMX: return go_norm_kind<DT, kMX>(a, gemma, CPL, st);
+    case kB128: return go_norm_kind<DT, kB128>(a, gemma, CPL, st);
+    default: return go_norm_kind<DT, kPT>(a, gemma, CPL, st);
     }
 }
 
@@ -483,19 +541,31 @@ int launch_norm(const NormPlan &p, void *stream)
     a.M = p.M;
     a.eps = p.eps;
     a.nseg = p.nseg;
-    a.gemma = p.kind;
     a.C0 = p.seg[0].chunks;
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
-    int NT, CPL;
-    row_config(a.C, NT, CPL);
+    const RowShapeRt sh = row_shape(a.C, p.M);
+    a.NT = sh.NT;
+    a.R = sh.R;
+    a.WPR = sh.WPR;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, NT, CPL, st)
-                                    : go_norm_mode<kBF16>(a, p.mode, NT, CPL, st);
+    const bool gemma = p.kind == 1;
+    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, sh.CPL, st)
+                                    : go_norm_mode<kBF16>(a, p.mode, gemma, sh.CPL, st);
     return (int)e;
 }
 
-// Chunks per lane of the flat kernels.
-constexpr int kFlatCPL = 2;
+// Chunks per lane of the flat kernels: one when the launch is small (a
+// lane's chunks are processed one after the other), more when there are
+// enough chunks to fill the GPU several times over.
+static int flat_cpl(int64_t total_chunks) { return total_chunks <= (int64_t)256 * 256 * 4 ? 1 : 2; }
+
+template <int MODE, int CPL>
+static hipError_t go_act(const ActArgs &a, hipStream_t st)
+{
+    const int64_t blocks = (a.total + 256 * CPL - 1) / (256 * CPL);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 
 int launch_act(const ActPlan &p, void *stream)
 {
@@ -509,41 +579,48 @@ int launch_act(const ActPlan &p, void *stream)
     a.I = p.I;
     a.total = p.M * (int64_t)a.C;
     a.invC = 1.0 / (double)a.C;
-    const int64_t blocks = (a.total + 256 * kFlatCPL - 1) / (256 * kFlatCPL);
     hipStream_t st = (hipStream_t)stream;
-    if (p.mode == kMX)
-        hipLaunchKernelGGL((act_quant_kernel<kMX, kFlatCPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((act_quant_kernel<kB128, kFlatCPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    return (int)hipGetLastError();
+    const int cpl = flat_cpl(a.total);
+    hipError_t e;
+    if (p.mode == kMX) e = cpl == 1 ? go_act<kMX, 1>(a, st) : go_act<kMX, 2>(a, st);
+    else e = cpl == 1 ? go_act<kB128, 1>(a, st) : go_act<kB128, 2>(a, st);
+    return (int)e;
+}
+
+template <int DT, int MODE, int CPL>
+static hipError_t go_quant_flat(const QuantArgs &a, hipStream_t st)
+{
+    const int64_t blocks = (a.total + 256 * CPL - 1) / (256 * CPL);
+    hipLaunchKernelGGL((quant_flat_kernel<DT, MODE, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int CPL>
+static hipError_t go_quant_row(const QuantArgs &a, hipStream_t st)
+{
+    const int64_t blocks = (a.M + a.R - 1) / a.R;
+    hipLaunchKernelGGL((quant_row_kernel<DT, CPL>), dim3((unsigned)blocks), dim3(a.NT * a.R), 0, st, a);
+    return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t go_quant(const QuantArgs &a, int mode, hipStream_t st)
+static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
 {
     if (mode == kPT) {
-        int NT, CPL;
-        row_config(a.C, NT, CPL);
-        // the row kernel covers up to 4 chunks per lane
-        auto launch = [&](auto kern, int nt) {
-            const int bs = nt < 256 ? 256 : nt;
-            const int64_t R = bs / nt;
-            hipLaunchKernelGGL(kern, dim3((unsigned)((a.M + R - 1) / R)), dim3(bs), 0, st, a);
-        };
-#define AFQ_QROW(NT_, CPL_) \
-        if (NT == NT_ && CPL == CPL_) { launch(quant_row_kernel<DT, NT_, CPL_>, NT_); return hipGetLastError(); }
-#define AFQ_QROW4(NT_) AFQ_QROW(NT_, 1) AFQ_QROW(NT_, 2) AFQ_QROW(NT_, 3) AFQ_QROW(NT_, 4)
-        AFQ_QROW4(64) AFQ_QROW4(128) AFQ_QROW4(256) AFQ_QROW4(512) AFQ_QROW4(1024)
-#undef AFQ_QROW4
-#undef AFQ_QROW
-        return hipErrorInvalidValue;
+        const RowShapeRt sh = row_shape(a.C, a.M);
+        a.NT = sh.NT;
+        a.R = sh.R;
+        a.WPR = sh.WPR;
+        switch (sh.CPL) {
+        case 1: return go_quant_row<DT, 1>(a, st);
+        case 2: return go_quant_row<DT, 2>(a, st);
+        case 3: return go_quant_row<DT, 3>(a, st);
+        default: return go_quant_row<DT, 4>(a, st);
+        }
     }
-    const int64_t blocks = (a.total + 256 * kFlatCPL - 1) / (256 * kFlatCPL);
-    if (mode == kMX)
-        hipLaunchKernelGGL((quant_flat_kernel<DT, kMX, kFlatCPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((quant_flat_kernel<DT, kB128, kFlatCPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    return hipGetLastError();
+    const bool one = flat_cpl(a.total) == 1;
+    if (mode == kMX) return one ? go_quant_flat<DT, kMX, 1>(a, st) : go_quant_flat<DT, kMX, 2>(a, st);
+    return one ? go_quant_flat<DT, kB128, 1>(a, st) : go_quant_flat<DT, kB128, 2>(a, st);
 }
 
 int launch_quant(const QuantPlan &p, void *stream)
@@ -558,6 +635,7 @@ int launch_quant(const QuantPlan &p, void *stream)
     a.cols = p.cols;
     a.total = p.M * (int64_t)a.C;
     a.invC = 1.0 / (double)a.C;
+    a.NT = a.R = a.WPR = 0;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (p.dtype == kFP32) e = go_quant<kFP32>(a, p.mode, st);
