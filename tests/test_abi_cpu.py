@@ -1,0 +1,180 @@
+"""The C ABI on the CPU: libafq.so loads, exports every function that
+include/afq.h declares, the Python binding's descriptor layouts match the C
+header, and every validation error is reported without touching a GPU
+(rejected calls return before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import activation_fp8_quant_amd as afq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "afq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant", "afq_status_string",
+            "afq_abi_version", "afq_last_hip_error"} <= set(names)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", afq.library_path], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = afq.load()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings():
+    assert afq.abi_version() == 1
+    for st in range(0, -9, -1):
+        s = afq.status_string(st)
+        assert s and s != "unknown status"
+    assert afq.status_string(-100) == "unknown status"
+    assert afq.load().afq_last_hip_error() == 0
+
+
+def test_descriptor_layout_matches_header(tmp_path):
+    """Compile a C probe against include/afq.h and compare sizes/offsets."""
+    probe = tmp_path / "probe.c"
+    fields = {
+        "afq_qact": ["values", "scales", "normed"],
+        "afq_norm_seg": ["x", "x_row_stride", "weight", "cols", "out"],
+        "afq_norm_desc": ["M", "nseg", "kind", "dtype", "mode", "eps", "reserved", "residual_in",
+                          "residual_out", "seg"],
+        "afq_act_desc": ["M", "I", "gate_up", "gate_up_row_stride", "mode", "reserved", "out"],
+        "afq_quant_desc": ["M", "cols", "x", "x_row_stride", "dtype", "mode", "out"],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "afq.h"', "int main(void){"]
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} size %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines.append("return 0;}")
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-std=c11", f"-I{ROOT}/include", str(probe), "-o", str(exe)])
+    c = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        parts = line.split()
+        c[tuple(parts[:-1])] = int(parts[-1])
+    py = {"afq_qact": afq._QAct, "afq_norm_seg": afq._NormSeg, "afq_norm_desc": afq._NormDesc,
+          "afq_act_desc": afq._ActDesc, "afq_quant_desc": afq._QuantDesc}
+    for st, cls in py.items():
+        assert c[(st, "size")] == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert c[(st, f)] == getattr(cls, f).offset, (st, f)
+
+
+# ------------------------------------------------------------- validation
+A16 = 0x10000  # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+def _norm(M=4, cols=256, mode=afq.MXFP8, **kw):
+    d = afq._NormDesc()
+    d.M, d.nseg, d.kind, d.dtype, d.mode, d.eps = M, 1, afq.GEMMA, 0, mode, 1e-6
+    s = d.seg[0]
+    s.x, s.x_row_stride, s.weight, s.cols = A16, cols, A16 * 2, cols
+    s.out.values, s.out.scales, s.out.normed = A16 * 3, A16 * 4, None
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _call_norm(d):
+    return afq.load().fused_add_rmsnorm_quant(ctypes.byref(d), None)
+
+
+def test_norm_validation_errors():
+    lib = afq.load()
+    assert lib.fused_add_rmsnorm_quant(None, None) == -1
+    assert _call_norm(_norm(M=-1)) == -2
+    assert _call_norm(_norm(cols=48)) == -2                    # not a multiple of 32 (MX)
+    assert _call_norm(_norm(cols=256 + 32, mode=afq.BLOCK128)) == -2
+    assert _call_norm(_norm(cols=65536)) == -2                 # above AFQ_MAX_COLS
+    assert _call_norm(_norm(nseg=3)) == -2
+    assert _call_norm(_norm(mode=7)) == -7
+    assert _call_norm(_norm(kind=5)) == -7
+    assert _call_norm(_norm(dtype=2)) == -4                    # fp32 norm input
+    assert _call_norm(_norm(eps=-1.0)) == -7
+    assert _call_norm(_norm(eps=float("nan"))) == -7
+    assert _call_norm(_norm(reserved=1)) == -7
+    d = _norm()
+    d.seg[0].x_row_stride = 128                                # stride < cols
+    assert _call_norm(d) == -2
+    d = _norm()
+    d.seg[0].x = None
+    assert _call_norm(d) == -1
+    d = _norm()
+    d.seg[0].x = A16 + 8                                       # misaligned
+    assert _call_norm(d) == -3
+    d = _norm()
+    d.seg[0].out.scales = A16 * 4 + 2                          # scales need 4-byte alignment
+    assert _call_norm(d) == -3
+    d = _norm()
+    d.residual_in = A16 * 8                                    # residual_in without residual_out
+    assert _call_norm(d) == -1
+    d = _norm(nseg=2)
+    d.seg[1] = d.seg[0]
+    d.residual_in, d.residual_out = A16 * 8, A16 * 9
+    assert _call_norm(d) == -2                                 # residual with two segments
+    d = _norm()
+    d.seg[0].out.scales = A16 * 3 + 64                         # scales inside the codes
+    assert _call_norm(d) == -5
+    d = _norm()
+    d.seg[0].out.values = A16                                  # codes over the input
+    assert _call_norm(d) == -5
+    d = _norm()
+    d.residual_in, d.residual_out = A16 * 8, A16 * 8 + 16      # partial residual overlap
+    assert _call_norm(d) == -5
+    # M == 0: OK and nothing enqueued, even with NULL pointers
+    d = _norm(M=0)
+    d.seg[0].x = None
+    assert _call_norm(d) == 0
+
+
+def test_act_and_quant_validation_errors():
+    lib = afq.load()
+    d = afq._ActDesc()
+    d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = 4, 768, A16, 1536, afq.MXFP8
+    d.out.values, d.out.scales = A16 * 64, A16 * 128
+    assert lib.silu_mul_quant(None, None) == -1
+    d.mode = afq.PER_TOKEN
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -6
+    d.mode = afq.BLOCK128                                       # 768 % 128 == 0 but ...
+    d.I = 96
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -2     # 96 % 128 != 0
+    d.I, d.gate_up_row_stride = 768, 1000
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -2     # stride < 2I
+    d.gate_up_row_stride = 1540
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -3     # pitch not 16-byte multiple
+    d.gate_up_row_stride = 1536
+    d.out.values = A16 + 32                                    # codes inside the input
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -5
+    q = afq._QuantDesc()
+    q.M, q.cols, q.x, q.x_row_stride, q.dtype, q.mode = 2, 256, A16, 256, 2, afq.MXFP8
+    q.out.values, q.out.scales = A16 * 64, A16 * 128
+    q.out.normed = A16 * 256
+    assert lib.fp8_quant(ctypes.byref(q), None) == -7          # no normed output here
+    q.out.normed = None
+    q.dtype = 9
+    assert lib.fp8_quant(ctypes.byref(q), None) == -7
+    q.dtype, q.cols = 2, 100
+    assert lib.fp8_quant(ctypes.byref(q), None) == -2
+
+
+def test_binding_refuses_without_library(monkeypatch):
+    """The binding fails loudly when libafq.so is missing (no fallback)."""
+    monkeypatch.setattr(afq, "_lib", None)
+    monkeypatch.setattr(afq, "library_path", "/nonexistent/libafq.so")
+    with pytest.raises(ImportError):
+        afq.load()
