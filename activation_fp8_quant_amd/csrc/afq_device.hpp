@@ -122,20 +122,30 @@ __device__ __forceinline__ float dppf(float v)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// max over the 4 lanes of a quad (an MXFP8 block); non-negative inputs
-__device__ __forceinline__ float max_quad(float v)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v)
 {
-    v = __builtin_fmaxf(v, dppf<kQuadSwap1>(v));
-    v = __builtin_fmaxf(v, dppf<kQuadSwap2>(v));
-    return v;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Maxima of non-negative floats are taken on their bit patterns (which
+// order like the values), as unsigned integer maxima: no NaN quieting is
+// needed, so each step is a single DPP-modified v_max_u32.
+// max over the 4 lanes of a quad (an MXFP8 block)
+__device__ __forceinline__ float max_quad(float f)
+{
+    uint32_t v = __float_as_uint(f);
+    v = max(v, dppu<kQuadSwap1>(v));
+    v = max(v, dppu<kQuadSwap2>(v));
+    return __uint_as_float(v);
 }
 // max over the 16 lanes of a DPP row (a 1x128 group)
-__device__ __forceinline__ float max_row16(float v)
+__device__ __forceinline__ float max_row16(float f)
 {
-    v = max_quad(v);
-    v = __builtin_fmaxf(v, dppf<kRowHalfMirror>(v));
-    v = __builtin_fmaxf(v, dppf<kRowMirror>(v));
-    return v;
+    uint32_t v = __float_as_uint(max_quad(f));
+    v = max(v, dppu<kRowHalfMirror>(v));
+    v = max(v, dppu<kRowMirror>(v));
+    return __uint_as_float(v);
 }
 // sum over the 16 lanes of a DPP row; every lane ends with the same value
 // (each step adds two partials that are equal across the pair, and fp32
@@ -148,20 +158,50 @@ __device__ __forceinline__ float sum_row16(float v)
     v += dppf<kRowMirror>(v);
     return v;
 }
-// all-reduce over the 64 lanes of a wavefront
-__device__ __forceinline__ float sum_wave(float v)
+// Exchange with the lane 16 (32) positions away: v_permlane16_swap /
+// v_permlane32_swap (gfx950) applied to two copies of v return, between
+// them, v of this lane and v of its partner; their sum (max) is symmetric,
+// so which copy is which does not matter.
+__device__ __forceinline__ float sum_xor16(float v)
 {
-    v = sum_row16(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
-__device__ __forceinline__ float max_wave(float v)
+__device__ __forceinline__ float sum_xor32(float v)
 {
-    v = max_row16(v);
-    v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
-    v = __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(max((uint32_t)p[0], (uint32_t)p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(max((uint32_t)p[0], (uint32_t)p[1]));
+}
+
+// all-reduce over the 64 lanes of a wavefront (no LDS traffic)
+__device__ __forceinline__ float sum_wave(float v) { return sum_xor32(sum_xor16(sum_row16(v))); }
+__device__ __forceinline__ float max_wave(float v) { return max_xor32(max_xor16(max_row16(v))); }
+
+// Block barrier that orders only LDS: the waves exchange reduction
+// partials through LDS, and their outstanding global stores need not
+// complete before the barrier (a __syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 1/sqrt(x) for x > 0: the hardware estimate and one Newton step.
+__device__ __forceinline__ float rsqrt_nr(float x)
+{
+    const float y = __builtin_amdgcn_rsqf(x);
+    return y * __builtin_fmaf(-0.5f * x, y * y, 1.5f);
 }
 
 // largest |u| of 8 values (v_max3_f32 with |.| source modifiers)
@@ -204,13 +244,27 @@ struct Fp32Scale {
     bool fast;  // s normal and 1/s finite
     bool zero;  // all-zero group
 };
+// For amax >= 2^-116 (s and 1/s normal): s = RN(amax/448) as a product
+// with RN(1/448) plus one Markstein correction, and RN(1/s) as the hardware
+// reciprocal plus one Newton correction.  Both equal the IEEE divisions on
+// every fp32 mantissa at every exponent of that range (checked on the GPU
+// over all 2^23 mantissas); smaller amax take the IEEE divisions.
 __device__ __forceinline__ Fp32Scale fp32_scale(float amax)
 {
     Fp32Scale sc;
-    sc.s = amax / 448.0f;          // IEEE division
     sc.zero = (amax == 0.0f);
-    sc.r = 1.0f / sc.s;            // IEEE division, correctly rounded
-    sc.fast = (sc.s >= 0x1p-126f) && (sc.r < 0x1p127f);
+    if (__builtin_expect(amax >= 0x1p-116f, 1)) {
+        constexpr float kInv448 = 1.0f / 448.0f;
+        const float s0 = amax * kInv448;
+        sc.s = __builtin_fmaf(__builtin_fmaf(-s0, 448.0f, amax), kInv448, s0);
+        const float r0 = __builtin_amdgcn_rcpf(sc.s);
+        sc.r = __builtin_fmaf(__builtin_fmaf(-sc.s, r0, 1.0f), r0, r0);
+        sc.fast = true;
+    } else {
+        sc.s = amax / 448.0f;      // IEEE division
+        sc.r = 1.0f / sc.s;        // IEEE division, correctly rounded
+        sc.fast = (sc.s >= 0x1p-126f) && (sc.r < 0x1p127f);
+    }
     return sc;
 }
 

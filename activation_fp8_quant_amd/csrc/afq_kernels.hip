@@ -39,6 +39,8 @@ struct NormArgs {
     int32_t NT;      // lanes per row
     int32_t R;       // rows per block
     int32_t WPR;     // wavefronts per row
+    float inv_cols0; // 1 / cols of each segment (the mean of the squares)
+    float inv_cols1;
 };
 
 template <int DT, int MODE, bool GEMMA, int CPL>
@@ -106,7 +108,7 @@ norm_quant_kernel(const NormArgs a)
             red[wave][0] = ss0;
             red[wave][1] = ss1;
         }
-        __syncthreads();
+        lds_barrier();
         ss0 = 0.f;
         ss1 = 0.f;
         for (int i = 0; i < a.WPR; ++i) {
@@ -114,8 +116,8 @@ norm_quant_kernel(const NormArgs a)
             ss1 += red[rib * a.WPR + i][1];
         }
     }
-    const float inv0 = 1.0f / __builtin_sqrtf(ss0 / (float)a.seg[0].cols + a.eps);
-    const float inv1 = a.nseg > 1 ? 1.0f / __builtin_sqrtf(ss1 / (float)a.seg[1].cols + a.eps) : 0.f;
+    const float inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
+    const float inv1 = a.nseg > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : 0.f;
 
     // ---- u = round_dt(h * inv * g), kept in place of h; optional copy
     float am0 = 0.f, am1 = 0.f;
@@ -146,7 +148,7 @@ norm_quant_kernel(const NormArgs a)
                 redm[wave][0] = am0;
                 redm[wave][1] = am1;
             }
-            __syncthreads();
+            lds_barrier();
             am0 = 0.f;
             am1 = 0.f;
             for (int i = 0; i < a.WPR; ++i) {
@@ -218,7 +220,7 @@ __device__ __forceinline__ float silu_fast(float g)
     constexpr float kL2eHi = 1.44269502162933349609375f;   // RN(log2 e)
     constexpr float kL2eLo = 1.925963033500011e-08f;       // log2 e - kL2eHi
     constexpr float kLn2 = 0.693147180559945309f;
-    const float gc = __builtin_fminf(g, 80.0f);
+    const float gc = g > 80.0f ? 80.0f : g;
     const float t = -gc * kL2eHi;
     const float tl = __builtin_fmaf(-gc, kL2eHi, -t) + (-gc) * kL2eLo;
     const float e0 = __builtin_amdgcn_exp2f(t);
@@ -256,12 +258,6 @@ __device__ __noinline__ float silu_f32_slow(float g)
     return (float)(hi + lo);
 }
 
-// fp32 silu for the MXFP8 path: the fast form, or fp64 where e^-g leaves
-// the fp32 range.
-__device__ __forceinline__ float silu_f32(float g)
-{
-    return g < -80.0f ? silu_f32_slow(g) : silu_fast(g);
-}
 
 // bf16 code of the two-term value hi + lo (lo a correction far below an
 // fp64 ulp of hi that only decides an exact midpoint of hi), sign given
@@ -298,17 +294,48 @@ __device__ __noinline__ uint32_t silu_bf16_slow(float g)
     return bf16_of_double2(hi, lo, (__float_as_uint(g) >> 16) & 0x8000u);
 }
 
-// bf16(silu(g)) for a bf16 gate, exactly rounded.  The fast fp32 value is
-// within a few ulp, so its bf16 rounding is the exact one unless it sits
-// within 16 fp32 ulps of a bf16 rounding midpoint, or e^-g leaves the fp32
-// range; those rare cases are redone in fp64.
-__device__ __forceinline__ float silu_bf16(float g)
+// bf16(silu(g)) of 8 bf16 gates, exactly rounded, as fp32 values.  The
+// fast fp32 value is within 2 ulp of silu(g) for every bf16 gate >= -80
+// (measured over all of them), so its bf16 rounding is the exact one unless
+// it sits within 3 fp32 ulps of a bf16 rounding midpoint; such gates, and
+// gates below -80 (e^-g beyond the fp32 range), are redone in fp64.  The
+// common path has no branch; a chunk holding a flagged gate (rare) takes
+// one.
+__device__ __forceinline__ void silu_bf16x8(const float (&g)[8], float (&s)[8])
 {
-    const float s = silu_fast(g);
-    const uint32_t low = __float_as_uint(s) & 0xFFFFu;
-    if (g < -80.0f || (low - (0x8000u - 16u)) <= 32u)
-        return __uint_as_float(silu_bf16_slow(g) << 16);
-    return bf16_lo(f32_to_bf16(s));
+    float raw[8];
+    uint32_t dmin = 0xFFFFFFFFu; // (low 16 bits) - (0x8000 - 3): <= 6 when within 3 ulps of a midpoint
+    float gmin = g[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        raw[i] = s[i] = silu_fast(g[i]);
+        dmin = min(dmin, (__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u));
+        gmin = __builtin_fminf(gmin, g[i]);
+    }
+    round8<kBF16>(s);
+    if (__builtin_expect(dmin <= 6u || gmin < -80.0f, 0)) {
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i)
+            if (g[i] < -80.0f || ((__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u)) <= 6u)
+                s[i] = __uint_as_float(silu_bf16_slow(g[i]) << 16);
+    }
+}
+
+// fp32 silu of 8 gates for the MXFP8 path: the fast form; gates below -80
+// (e^-g beyond the fp32 range) are redone in fp64.
+__device__ __forceinline__ void silu_f32x8(const float (&g)[8], float (&s)[8])
+{
+    float gmin = g[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] = silu_fast(g[i]);
+        gmin = __builtin_fminf(gmin, g[i]);
+    }
+    if (gmin < -80.0f) {
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i)
+            if (g[i] < -80.0f) s[i] = silu_f32_slow(g[i]);
+    }
 }
 
 template <int MODE, int CPL>
@@ -341,15 +368,19 @@ act_quant_kernel(const ActArgs a)
         const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
         uint2 q;
         if constexpr (MODE == kMX) {
+            float sg[8];
+            silu_f32x8(g, sg);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= silu_f32(g[i]);
+            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
             if (a.act) stg<uint4>(a.act + out_off * 2, pack8<kBF16>(v));
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
         } else {
+            float sg[8];
+            silu_bf16x8(g, sg);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= silu_bf16(g[i]);
+            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
             const uint4 ap = round8<kBF16>(v);
             if (a.act) stg<uint4>(a.act + out_off * 2, ap);
             const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
@@ -455,7 +486,7 @@ quant_row_kernel(const QuantArgs a)
     __shared__ float redm[kMaxBlock / 64];
     if (a.WPR > 1) {
         if ((tid & 63) == 0) redm[wave] = am;
-        __syncthreads();
+        lds_barrier();
         am = 0.f;
         for (int i = 0; i < a.WPR; ++i) am = __builtin_fmaxf(am, redm[rib * a.WPR + i]);
     }
@@ -473,18 +504,18 @@ quant_row_kernel(const QuantArgs a)
 // Row shape for a row of C chunks.  Few rows (latency-bound: every lane of
 // a row works through its chunks one after the other, so the row's time
 // grows with the chunks per lane): as many lanes as chunks, up to 1024.
-// Many rows (bandwidth-bound): about 256 lanes per row, at most 4 chunks
-// per lane.  NT is a whole number of wavefronts; rows of fewer than 256
-// lanes are packed several to a block.
+// Many rows (bandwidth-bound): two chunks per lane, which measured best or
+// within a few % of best on every configured width (hidden 6144 MX + copy,
+// 4096 1x128, the 1536 + 512 two-segment per-token rows).  NT is a whole
+// number of wavefronts; rows of fewer than 256 lanes are packed several to
+// a block.
 struct RowShapeRt {
     int NT, CPL, R, WPR;
 };
 static RowShapeRt row_shape(int C, int64_t M)
 {
     RowShapeRt s;
-    const bool few_rows = M <= 1024;
-    int cpl = few_rows ? (C + 1023) / 1024 : (C + 255) / 256;
-    cpl = cpl < 1 ? 1 : (cpl > 4 ? 4 : cpl);
+    int cpl = M <= 1024 ? 1 : 2;
     if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
     int nt = (C + cpl - 1) / cpl;
     nt = (nt + 63) / 64 * 64;
@@ -547,6 +578,8 @@ int launch_norm(const NormPlan &p, void *stream)
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;
+    a.inv_cols0 = 1.0f / (float)p.seg[0].cols;
+    a.inv_cols1 = 1.0f / (float)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
     hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, sh.CPL, st)
@@ -554,10 +587,9 @@ int launch_norm(const NormPlan &p, void *stream)
     return (int)e;
 }
 
-// Chunks per lane of the flat kernels: one when the launch is small (a
-// lane's chunks are processed one after the other), more when there are
-// enough chunks to fill the GPU several times over.
-static int flat_cpl(int64_t total_chunks) { return total_chunks <= (int64_t)256 * 256 * 4 ? 1 : 2; }
+// Chunks per lane of the flat kernels: one (measured best or equal for the
+// SiLU-and-mul widths 768, 3072 and 12288 at every row count).
+static int flat_cpl(int64_t) { return 1; }
 
 template <int MODE, int CPL>
 static hipError_t go_act(const ActArgs &a, hipStream_t st)

@@ -222,7 +222,7 @@ def rotation_sets(ws_bytes, target=1 << 30):
 
 
 # ----------------------------------------------------------------- CPU leg
-def cpu_baseline(rows=8192):
+def cpu_baseline(rows=16384):
     """The oracle, as it stands, on a bounded sample of the headline
     workload: `rows` rows of the M = 16384, H = 6144 batch, one oracle call
     per thread over a row range."""
