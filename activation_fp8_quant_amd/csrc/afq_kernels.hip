@@ -23,8 +23,10 @@ namespace afq {
 
 // ===================================================================== norm
 // Rows are NT lanes (a whole number of wavefronts, NT <= 1024); a block
-// holds R rows.  Both are launch parameters; the per-lane chunk count CPL
-// is a template parameter (the loops over a lane's chunks are unrolled).
+// holds R rows (R > 1 only for NT of 64 or 128 lanes).  Both are launch
+// parameters; the per-lane chunk count CPL and the segment count NSEG are
+// template parameters (the loops over a lane's chunks are unrolled, and a
+// single-segment row carries no segment selection).
 constexpr int kMaxBlock = 1024;
 
 struct NormArgs {
@@ -33,31 +35,48 @@ struct NormArgs {
     uint8_t *res_out;
     int64_t M;
     float eps;
-    int32_t nseg;
-    int32_t C0;      // chunks of segment 0
-    int32_t C;       // chunks of both segments
-    int32_t NT;      // lanes per row
-    int32_t R;       // rows per block
-    int32_t WPR;     // wavefronts per row
-    float inv_cols0; // 1 / cols of each segment (the mean of the squares)
+    int32_t C0;        // chunks of segment 0
+    int32_t C;         // chunks of both segments
+    int32_t NT;        // lanes per row
+    int32_t R;         // rows per block
+    int32_t WPR;       // wavefronts per row
+    int32_t wpr_shift; // log2(WPR) when R > 1
+    float inv_cols0;   // 1 / cols of each segment (the mean of the squares)
     float inv_cols1;
 };
 
-template <int DT, int MODE, bool GEMMA, int CPL>
+// sum of squares of the 8 values of a packed chunk (v_dot2 on pairs)
+template <int DT>
+__device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
+{
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (DT == kBF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
+                                                  __builtin_bit_cast(bf16x2, w[i]), acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]),
+                                         __builtin_bit_cast(f16x2, w[i]), acc, false);
+    }
+    return acc;
+}
+
+template <int DT, int MODE, bool GEMMA, int CPL, int NSEG>
 __global__ void __launch_bounds__(kMaxBlock)
 norm_quant_kernel(const NormArgs a)
 {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int rib = wave / a.WPR;            // row within the block
-    const int t = tid - rib * a.NT;          // lane within the row
+    const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
+    const int t = tid - rib * a.NT;                       // lane within the row
     const int64_t row = (int64_t)blockIdx.x * a.R + rib;
     const bool row_ok = row < a.M;
     const bool has_res = a.res_in != nullptr;
 
-    // per-row bases: x of each segment, the residual rows, and the output
-    // rows (codes, scales, copy) of each segment
-    const uint8_t *xrow[2] = {a.seg[0].x + row * a.seg[0].x_pitch, a.seg[1].x + row * a.seg[1].x_pitch};
+    // per-row bases
+    const uint8_t *xrow0 = a.seg[0].x + row * a.seg[0].x_pitch;
+    const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + row * a.seg[1].x_pitch : xrow0;
     const int64_t rrow = row * a.C0 * 16;
 
     // ---- issue every load of the row
@@ -68,10 +87,15 @@ norm_quant_kernel(const NormArgs a)
     for (int k = 0; k < CPL; ++k) {
         const int c = t + k * a.NT;
         ok[k] = row_ok && c < a.C;
-        sg[k] = c >= a.C0 ? 1 : 0;
-        lc[k] = c - (sg[k] ? a.C0 : 0);
+        if constexpr (NSEG == 1) {
+            sg[k] = 0;
+            lc[k] = c;
+        } else {
+            sg[k] = c >= a.C0 ? 1 : 0;
+            lc[k] = c - (sg[k] ? a.C0 : 0);
+        }
         if (ok[k]) {
-            xv[k] = ldg<uint4>((sg[k] ? xrow[1] : xrow[0]) + lc[k] * 16);
+            xv[k] = ldg<uint4>((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
             wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
             if (has_res)
                 rv[k] = ldg<uint4>(a.res_in + rrow + lc[k] * 16);
@@ -84,80 +108,85 @@ norm_quant_kernel(const NormArgs a)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
-        unpack8<DT>(xv[k], h[k]);
+        uint4 hp = xv[k];
         if (has_res) {
             float rf[8];
+            unpack8<DT>(xv[k], h[k]);
             unpack8<DT>(rv[k], rf);
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
-            stg<uint4>(a.res_out + rrow + lc[k] * 16, round8<DT>(h[k]));
+            hp = pack8<DT>(h[k]);
+            stg<uint4>(a.res_out + rrow + lc[k] * 16, hp);
         }
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p = __builtin_fmaf(h[k][i], h[k][i], p);
-        if (sg[k]) ss1 += p; else ss0 += p;
+        unpack8<DT>(hp, h[k]);
+        if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
+        else ss0 = sumsq8<DT>(hp, ss0);
     }
 
-    // ---- row reduction: DPP inside the wavefront, LDS across wavefronts
+    // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
+    //      across the wavefronts of the row
     __shared__ float red[kMaxBlock / 64][2];
     __shared__ float redm[kMaxBlock / 64][2];
     ss0 = sum_wave(ss0);
-    if (a.nseg > 1) ss1 = sum_wave(ss1);
+    if constexpr (NSEG > 1) ss1 = sum_wave(ss1);
     if (a.WPR > 1) {
         if ((tid & 63) == 0) {
             red[wave][0] = ss0;
-            red[wave][1] = ss1;
+            if constexpr (NSEG > 1) red[wave][1] = ss1;
         }
         lds_barrier();
         ss0 = 0.f;
         ss1 = 0.f;
         for (int i = 0; i < a.WPR; ++i) {
             ss0 += red[rib * a.WPR + i][0];
-            ss1 += red[rib * a.WPR + i][1];
+            if constexpr (NSEG > 1) ss1 += red[rib * a.WPR + i][1];
         }
     }
     const float inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
-    const float inv1 = a.nseg > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : 0.f;
+    const float inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
 
-    // ---- u = round_dt(h * inv * g), kept in place of h; optional copy
+    // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
+    //      Gemma: g * inv = (1 + w) inv as one FMA.
     float am0 = 0.f, am1 = 0.f;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
-        const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
         const float inv = sg[k] ? inv1 : inv0;
         float wf[8];
         unpack8<DT>(wv[k], wf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[k][i] = (h[k][i] * inv) * (GEMMA ? 1.0f + wf[i] : wf[i]);
+        for (int i = 0; i < 8; ++i)
+            h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
         const uint4 up = round8<DT>(h[k]);
-        if (s.normed)
-            stg<uint4>(s.normed + (row * s.cols + (int64_t)lc[k] * 8) * 2, up);
+        uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
+        const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
+        if (normed)
+            stg<uint4>(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
         if constexpr (MODE == kPT) {
             const float m = amax8(h[k]);
-            if (sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
+            if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
         }
     }
 
     // ---- quantise
     if constexpr (MODE == kPT) {
         am0 = max_wave(am0);
-        if (a.nseg > 1) am1 = max_wave(am1);
+        if constexpr (NSEG > 1) am1 = max_wave(am1);
         if (a.WPR > 1) {
             if ((tid & 63) == 0) {
                 redm[wave][0] = am0;
-                redm[wave][1] = am1;
+                if constexpr (NSEG > 1) redm[wave][1] = am1;
             }
             lds_barrier();
             am0 = 0.f;
             am1 = 0.f;
             for (int i = 0; i < a.WPR; ++i) {
                 am0 = __builtin_fmaxf(am0, redm[rib * a.WPR + i][0]);
-                am1 = __builtin_fmaxf(am1, redm[rib * a.WPR + i][1]);
+                if constexpr (NSEG > 1) am1 = __builtin_fmaxf(am1, redm[rib * a.WPR + i][1]);
             }
         }
         const Fp32Scale sc0 = fp32_scale(am0);
-        const Fp32Scale sc1 = fp32_scale(am1);
+        const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
             if (!ok[k]) continue;
@@ -527,38 +556,43 @@ static RowShapeRt row_shape(int C, int64_t M)
 }
 
 template <int DT, int MODE, bool GEMMA, int CPL>
-static hipError_t go_norm(const NormArgs &a, hipStream_t st)
+static hipError_t go_norm(const NormArgs &a, int nseg, hipStream_t st)
 {
     const int64_t blocks = (a.M + a.R - 1) / a.R;
-    hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL>), dim3((unsigned)blocks),
-                       dim3(a.NT * a.R), 0, st, a);
+    if (nseg > 1)
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2>), dim3((unsigned)blocks),
+                           dim3(a.NT * a.R), 0, st, a);
+    else
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1>), dim3((unsigned)blocks),
+                           dim3(a.NT * a.R), 0, st, a);
     return hipGetLastError();
 }
 
 template <int DT, int MODE, bool GEMMA>
-static hipError_t go_norm_cpl(const NormArgs &a, int CPL, hipStream_t st)
+static hipError_t go_norm_cpl(const NormArgs &a, int nseg, int CPL, hipStream_t st)
 {
     switch (CPL) {
-    case 1: return go_norm<DT, MODE, GEMMA, 1>(a, st);
-    case 2: return go_norm<DT, MODE, GEMMA, 2>(a, st);
-    case 3: return go_norm<DT, MODE, GEMMA, 3>(a, st);
-    default: return go_norm<DT, MODE, GEMMA, 4>(a, st);
+    case 1: return go_norm<DT, MODE, GEMMA, 1>(a, nseg, st);
+    case 2: return go_norm<DT, MODE, GEMMA, 2>(a, nseg, st);
+    case 3: return go_norm<DT, MODE, GEMMA, 3>(a, nseg, st);
+    default: return go_norm<DT, MODE, GEMMA, 4>(a, nseg, st);
     }
 }
 
 template <int DT, int MODE>
-static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int CPL, hipStream_t st)
+static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int nseg, int CPL, hipStream_t st)
 {
-    return gemma ? go_norm_cpl<DT, MODE, true>(a, CPL, st) : go_norm_cpl<DT, MODE, false>(a, CPL, st);
+    return gemma ? go_norm_cpl<DT, MODE, true>(a, nseg, CPL, st)
+                 : go_norm_cpl<DT, MODE, false>(a, nseg, CPL, st);
 }
 
 template <int DT>
-static hipError_t go_norm_mode(const NormArgs &a, int mode, bool gemma, int CPL, hipStream_t st)
+static hipError_t go_norm_mode(const NormArgs &a, int mode, bool gemma, int nseg, int CPL, hipStream_t st)
 {
     switch (mode) {
-    case kMX: return go_norm_kind<DT, kMX>(a, gemma, CPL, st);
-    case kB128: return go_norm_kind<DT, kB128>(a, gemma, CPL, st);
-    default: return go_norm_kind<DT, kPT>(a, gemma, CPL, st);
+    case kMX: return go_norm_kind<DT, kMX>(a, gemma, nseg, CPL, st);
+    case kB128: return go_norm_kind<DT, kB128>(a, gemma, nseg, CPL, st);
+    default: return go_norm_kind<DT, kPT>(a, gemma, nseg, CPL, st);
     }
 }
 
@@ -571,19 +605,19 @@ int launch_norm(const NormPlan &p, void *stream)
     a.res_out = p.res_out;
     a.M = p.M;
     a.eps = p.eps;
-    a.nseg = p.nseg;
     a.C0 = p.seg[0].chunks;
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
     const RowShapeRt sh = row_shape(a.C, p.M);
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;
+    a.wpr_shift = sh.WPR == 2 ? 1 : 0; // R > 1 only with one or two wavefronts per row
     a.inv_cols0 = 1.0f / (float)p.seg[0].cols;
     a.inv_cols1 = 1.0f / (float)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
-    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, sh.CPL, st)
-                                    : go_norm_mode<kBF16>(a, p.mode, gemma, sh.CPL, st);
+    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, p.nseg, sh.CPL, st)
+                                    : go_norm_mode<kBF16>(a, p.mode, gemma, p.nseg, sh.CPL, st);
     return (int)e;
 }
 
