@@ -217,26 +217,39 @@ norm_quant_kernel(const NormArgs a)
 }
 
 // ============================================================ SiLU-and-mul
+// Division of a flat 32-bit chunk index by the chunks per row C, by a
+// multiplier computed on the host (round-up method): with l = ceil(log2 C)
+// and m = floor(2^32 (2^l - C) / C) + 1, n / C = (mulhi(n, m) + n) >> l
+// for every n < 2^32 (the sum is taken in 64 bits).
+struct DivC {
+    uint32_t m;
+    uint32_t l;
+};
+static DivC divc(uint32_t C)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < C) ++l;
+    DivC d;
+    d.m = (uint32_t)(((1ull << 32) * ((1ull << l) - C)) / C + 1);
+    d.l = l;
+    return d;
+}
+__device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
+{
+    return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
+}
+
 struct ActArgs {
     const uint8_t *gu;
     int64_t gu_pitch;
     uint8_t *values;
     uint8_t *scales;
     uint8_t *act;
-    int64_t total;    // M * C chunks
+    uint32_t total;   // chunks of this launch (rows * C), < 2^32
     int32_t C;        // chunks per row (I / 8)
     int32_t I;
-    double invC;      // 1 / C, for the row index of a flat chunk
+    DivC dc;          // division by C
 };
-
-// Row of flat chunk f: an fp64 estimate corrected by at most one step.
-__device__ __forceinline__ int64_t row_of(int64_t f, int32_t C, double invC)
-{
-    int64_t r = (int64_t)((double)f * invC);
-    if (r * C > f) --r;
-    else if ((r + 1) * C <= f) ++r;
-    return r;
-}
 
 // silu(g) = g / (1 + e^-g) in fp32 for g >= -80, within a few ulp:
 // e^-g = 2^t with t = -g log2(e) carried as hi + lo (the product's exact
@@ -371,17 +384,18 @@ template <int MODE, int CPL>
 __global__ void __launch_bounds__(256)
 act_quant_kernel(const ActArgs a)
 {
-    const int64_t base = (int64_t)blockIdx.x * (256 * CPL) + threadIdx.x;
+    const uint32_t base = blockIdx.x * (256u * CPL) + threadIdx.x;
     uint4 gv[CPL], uv[CPL];
     bool ok[CPL];
     int64_t rw[CPL];
     int32_t lc[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
-        const int64_t f = base + k * 256;
+        const uint32_t f = base + k * 256u;
         ok[k] = f < a.total;
-        rw[k] = row_of(f, a.C, a.invC);
-        lc[k] = (int32_t)(f - rw[k] * a.C);
+        const uint32_t r = div_c(f, a.dc);
+        rw[k] = r;
+        lc[k] = (int32_t)(f - r * (uint32_t)a.C);
         if (ok[k]) {
             const uint8_t *p = a.gu + rw[k] * a.gu_pitch + (int64_t)lc[k] * 16;
             gv[k] = ldg<uint4>(p);
@@ -427,11 +441,11 @@ struct QuantArgs {
     int64_t x_pitch;
     uint8_t *values;
     uint8_t *scales;
-    int64_t total;   // M * C chunks (flat kernel)
+    uint32_t total;  // chunks of this launch (flat kernel), < 2^32
     int64_t M;
     int32_t C;       // chunks per row
     int32_t cols;
-    double invC;
+    DivC dc;         // division by C
     int32_t NT;      // lanes per row (row kernel)
     int32_t R;       // rows per block (row kernel)
     int32_t WPR;     // wavefronts per row (row kernel)
@@ -456,17 +470,18 @@ __global__ void __launch_bounds__(256)
 quant_flat_kernel(const QuantArgs a)
 {
     constexpr int EB = DT == kFP32 ? 4 : 2;
-    const int64_t base = (int64_t)blockIdx.x * (256 * CPL) + threadIdx.x;
+    const uint32_t base = blockIdx.x * (256u * CPL) + threadIdx.x;
     float v[CPL][8];
     bool ok[CPL];
     int64_t rw[CPL];
     int32_t lc[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
-        const int64_t f = base + k * 256;
+        const uint32_t f = base + k * 256u;
         ok[k] = f < a.total;
-        rw[k] = row_of(f, a.C, a.invC);
-        lc[k] = (int32_t)(f - rw[k] * a.C);
+        const uint32_t r = div_c(f, a.dc);
+        rw[k] = r;
+        lc[k] = (int32_t)(f - r * (uint32_t)a.C);
         if (ok[k]) load_chunk<DT>(a.x + rw[k] * a.x_pitch + (int64_t)lc[k] * 8 * EB, v[k]);
     }
 #pragma unroll
@@ -621,43 +636,46 @@ int launch_norm(const NormPlan &p, void *stream)
     return (int)e;
 }
 
-// Chunks per lane of the flat kernels: one (measured best or equal for the
-// SiLU-and-mul widths 768, 3072 and 12288 at every row count).
-static int flat_cpl(int64_t) { return 1; }
-
 template <int MODE, int CPL>
 static hipError_t go_act(const ActArgs &a, hipStream_t st)
 {
-    const int64_t blocks = (a.total + 256 * CPL - 1) / (256 * CPL);
-    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
+// Rows per launch of the flat kernels: the flat chunk index stays below
+// 2^31 (larger M is covered by several launches over row slices).
+static int64_t flat_rows_per_launch(int32_t C) { return ((int64_t)1 << 31) / C; }
+
 int launch_act(const ActPlan &p, void *stream)
 {
-    ActArgs a;
-    a.gu = p.gu;
-    a.gu_pitch = p.gu_pitch;
-    a.values = p.values;
-    a.scales = p.scales;
-    a.act = p.act;
-    a.C = p.I / 8;
-    a.I = p.I;
-    a.total = p.M * (int64_t)a.C;
-    a.invC = 1.0 / (double)a.C;
     hipStream_t st = (hipStream_t)stream;
-    const int cpl = flat_cpl(a.total);
-    hipError_t e;
-    if (p.mode == kMX) e = cpl == 1 ? go_act<kMX, 1>(a, st) : go_act<kMX, 2>(a, st);
-    else e = cpl == 1 ? go_act<kB128, 1>(a, st) : go_act<kB128, 2>(a, st);
-    return (int)e;
+    const int32_t C = p.I / 8;
+    const int64_t step = flat_rows_per_launch(C);
+    for (int64_t r0 = 0; r0 < p.M; r0 += step) {
+        const int64_t rows = p.M - r0 < step ? p.M - r0 : step;
+        ActArgs a;
+        a.gu = p.gu + r0 * p.gu_pitch;
+        a.gu_pitch = p.gu_pitch;
+        a.values = p.values + r0 * p.I;
+        a.scales = p.scales + r0 * (p.mode == kMX ? p.I / 32 : 4 * (p.I / 128));
+        a.act = p.act ? p.act + r0 * p.I * 2 : nullptr;
+        a.C = C;
+        a.I = p.I;
+        a.total = (uint32_t)(rows * C);
+        a.dc = divc((uint32_t)C);
+        hipError_t e = p.mode == kMX ? go_act<kMX, 1>(a, st) : go_act<kB128, 1>(a, st);
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
 }
 
 template <int DT, int MODE, int CPL>
 static hipError_t go_quant_flat(const QuantArgs &a, hipStream_t st)
 {
-    const int64_t blocks = (a.total + 256 * CPL - 1) / (256 * CPL);
-    hipLaunchKernelGGL((quant_flat_kernel<DT, MODE, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
+    hipLaunchKernelGGL((quant_flat_kernel<DT, MODE, CPL>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -684,9 +702,24 @@ static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
         default: return go_quant_row<DT, 4>(a, st);
         }
     }
-    const bool one = flat_cpl(a.total) == 1;
-    if (mode == kMX) return one ? go_quant_flat<DT, kMX, 1>(a, st) : go_quant_flat<DT, kMX, 2>(a, st);
-    return one ? go_quant_flat<DT, kB128, 1>(a, st) : go_quant_flat<DT, kB128, 2>(a, st);
+    // flat kernels over row slices of at most 2^31 chunks
+    constexpr int EB = DT == kFP32 ? 4 : 2;
+    const int64_t step = flat_rows_per_launch(a.C);
+    const int64_t sbytes = mode == kMX ? a.cols / 32 : 4 * (a.cols / 128);
+    QuantArgs b = a;
+    b.dc = divc((uint32_t)a.C);
+    for (int64_t r0 = 0; r0 < a.M; r0 += step) {
+        const int64_t rows = a.M - r0 < step ? a.M - r0 : step;
+        b.x = a.x + r0 * a.x_pitch;
+        b.values = a.values + r0 * a.cols;
+        b.scales = a.scales + r0 * sbytes;
+        b.M = rows;
+        b.total = (uint32_t)(rows * a.C);
+        const hipError_t e = mode == kMX ? go_quant_flat<DT, kMX, 1>(b, st) : go_quant_flat<DT, kB128, 1>(b, st);
+        if (e != hipSuccess) return e;
+    }
+    (void)EB;
+    return hipSuccess;
 }
 
 int launch_quant(const QuantPlan &p, void *stream)
@@ -699,8 +732,8 @@ int launch_quant(const QuantPlan &p, void *stream)
     a.M = p.M;
     a.C = p.cols / 8;
     a.cols = p.cols;
-    a.total = p.M * (int64_t)a.C;
-    a.invC = 1.0 / (double)a.C;
+    a.total = 0;
+    a.dc = DivC{0, 0};
     a.NT = a.R = a.WPR = 0;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
