@@ -95,10 +95,10 @@ norm_quant_kernel(const NormArgs a)
             lc[k] = c - (sg[k] ? a.C0 : 0);
         }
         if (ok[k]) {
-            xv[k] = ldg<uint4>((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
+            xv[k] = ldg_stream((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
             wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
             if (has_res)
-                rv[k] = ldg<uint4>(a.res_in + rrow + lc[k] * 16);
+                rv[k] = ldg_stream(a.res_in + rrow + lc[k] * 16);
         }
     }
 
@@ -116,7 +116,7 @@ norm_quant_kernel(const NormArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
             hp = pack8<DT>(h[k]);
-            stg<uint4>(a.res_out + rrow + lc[k] * 16, hp);
+            stg_stream(a.res_out + rrow + lc[k] * 16, hp);
         }
         unpack8<DT>(hp, h[k]);
         if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
@@ -161,7 +161,7 @@ norm_quant_kernel(const NormArgs a)
         uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
         const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
         if (normed)
-            stg<uint4>(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
+            stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
         if constexpr (MODE == kPT) {
             const float m = amax8(h[k]);
             if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
@@ -192,7 +192,7 @@ norm_quant_kernel(const NormArgs a)
             if (!ok[k]) continue;
             const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
             const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
-            stg<uint2>(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
             if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
         }
     } else {
@@ -211,7 +211,7 @@ norm_quant_kernel(const NormArgs a)
                 if ((lc[k] & 15) == 0)
                     reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
             }
-            stg<uint2>(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
         }
     }
 }
@@ -398,8 +398,8 @@ act_quant_kernel(const ActArgs a)
         lc[k] = (int32_t)(f - r * (uint32_t)a.C);
         if (ok[k]) {
             const uint8_t *p = a.gu + rw[k] * a.gu_pitch + (int64_t)lc[k] * 16;
-            gv[k] = ldg<uint4>(p);
-            uv[k] = ldg<uint4>(p + (int64_t)a.I * 2);
+            gv[k] = ldg_stream(p);
+            uv[k] = ldg_stream(p + (int64_t)a.I * 2);
         }
     }
 #pragma unroll
@@ -415,7 +415,7 @@ act_quant_kernel(const ActArgs a)
             silu_f32x8(g, sg);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] *= sg[i];
-            if (a.act) stg<uint4>(a.act + out_off * 2, pack8<kBF16>(v));
+            if (a.act) stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
@@ -425,13 +425,13 @@ act_quant_kernel(const ActArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] *= sg[i];
             const uint4 ap = round8<kBF16>(v);
-            if (a.act) stg<uint4>(a.act + out_off * 2, ap);
+            if (a.act) stg_stream(a.act + out_off * 2, ap);
             const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
             q = fp32scale_codes8(v, sc);
             if ((lc[k] & 15) == 0)
                 reinterpret_cast<float *>(a.scales)[rw[k] * (a.I / 128) + lc[k] / 16] = sc.s;
         }
-        stg<uint2>(a.values + out_off, q);
+        stg_stream(a.values + out_off, q);
     }
 }
 
@@ -455,13 +455,13 @@ template <int DT>
 __device__ __forceinline__ void load_chunk(const uint8_t *p, float (&v)[8])
 {
     if constexpr (DT == kFP32) {
-        const uint4 a = ldg<uint4>(p), b = ldg<uint4>(p + 16);
+        const uint4 a = ldg_stream(p), b = ldg_stream(p + 16);
         v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
         v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
         v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
         v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
     } else {
-        unpack8<DT>(ldg<uint4>(p), v);
+        unpack8<DT>(ldg_stream(p), v);
     }
 }
 
@@ -499,7 +499,7 @@ quant_flat_kernel(const QuantArgs a)
             if ((lc[k] & 15) == 0)
                 reinterpret_cast<float *>(a.scales)[rw[k] * (a.cols / 128) + lc[k] / 16] = sc.s;
         }
-        stg<uint2>(a.values + out_off, q);
+        stg_stream(a.values + out_off, q);
     }
 }
 
@@ -539,7 +539,7 @@ quant_row_kernel(const QuantArgs a)
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
         const int c = t + k * a.NT;
-        stg<uint2>(a.values + row * a.cols + (int64_t)c * 8, fp32scale_codes8(v[k], sc));
+        stg_stream(a.values + row * a.cols + (int64_t)c * 8, fp32scale_codes8(v[k], sc));
         if (c == 0) reinterpret_cast<float *>(a.scales)[row] = sc.s;
     }
 }
