@@ -48,7 +48,7 @@
  * SiLU-and-mul (silu_mul_quant), per element j of a row:
  *   MXFP8:    a_j = fp32(silu(gate_j) * up_j), quantised without any bf16
  *             rounding (vLLM pull request 65478, "Purpose", commit 2: the
- *             fp32 swiglu + quant in one pass)
+ *             activation stays fp32 between SiLU-and-mul and the quantiser)
  *   BLOCK128: a_j = bf16(bf16(silu(gate_j)) * up_j), the rounding of the
  *             unfused SiluAndMul, so the codes equal the unfused chain
  *             (SGLang pull request 48043, "Modifications")

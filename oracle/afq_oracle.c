@@ -398,9 +398,9 @@ double orc_silu(double g)
  * the fp32 activation straight into the quantiser, with no bf16 rounding):
  *     a_j = fl32(silu(g_j) * u_j)    (exact product rounded once to fp32)
  *     scale from the fp32 block amax, codes e4m3(clamp(a_j / X)).
- * BLOCK128 ([P2] "Modifications": the fused kernel rounds like the unfused
- * SiluAndMul, silu to bf16 and then the product to bf16, so it equals the
- * unfused path):
+ * BLOCK128 ([P2] "Modifications": the fused kernel takes the same two bf16
+ * roundings as the unfused SiLU-and-mul, silu first and then the product,
+ * so its output equals the unfused path):
  *     a_j = RNE_bf16(RNE_bf16(silu(g_j)) * u_j), then the 1x128 quant.
  * The pages pair SiLU-and-mul with no per-token quant; that mode is rejected
  * (returns -1).  act_out (optional) receives RNE_bf16(a_j).
