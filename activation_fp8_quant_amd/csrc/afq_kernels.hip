@@ -251,22 +251,21 @@ struct ActArgs {
     DivC dc;          // division by C
 };
 
-// silu(g) = g / (1 + e^-g) in fp32 for g >= -80, within a few ulp:
-// e^-g = 2^t with t = -g log2(e) carried as hi + lo (the product's exact
-// rounding error by FMA plus the tail of log2(e)), 2^t = exp2(hi) (1 + lo
-// ln2) with the hardware exp2, then g times the hardware reciprocal.  For
-// g > 80, e^-g < 2^-115 vanishes next to 1 either way, so the exponent is
-// taken at min(g, 80) (keeps -g log2(e) finite for the largest gates).
+// silu(g) = g / (1 + e^-g) in fp32 for a bf16 gate g >= -80, within 2 ulp
+// of the fp64 value (measured over every such gate).  log2(e) is split as
+// kHi + kLo with a 16-bit head, so t = -g kHi is exact for a bf16 g and
+// e^-g = 2^t e^y with y = -g kLo ln 2 (|y| < 4e-4 for |g| <= 80); the
+// hardware exp2 gives 2^t and e^y is taken to first order.  For large
+// positive g, 2^t vanishes and y is clamped so that the product stays
+// finite.  Then g times the hardware reciprocal of 1 + e^-g.
 __device__ __forceinline__ float silu_fast(float g)
 {
-    constexpr float kL2eHi = 1.44269502162933349609375f;   // RN(log2 e)
-    constexpr float kL2eLo = 1.925963033500011e-08f;       // log2 e - kL2eHi
-    constexpr float kLn2 = 0.693147180559945309f;
-    const float gc = g > 80.0f ? 80.0f : g;
-    const float t = -gc * kL2eHi;
-    const float tl = __builtin_fmaf(-gc, kL2eHi, -t) + (-gc) * kL2eLo;
+    constexpr float kHi = 1.44268798828125f;    // log2(e) to 16 significant bits
+    constexpr float kLoLn2 = 4.8884954e-06f;    // (log2(e) - kHi) ln 2
+    const float t = g * -kHi;
+    const float y = __builtin_fmaxf(g * -kLoLn2, -0.01f);
     const float e0 = __builtin_amdgcn_exp2f(t);
-    const float e = __builtin_fmaf(e0, tl * kLn2, e0);
+    const float e = __builtin_fmaf(e0, y, e0);
     return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
