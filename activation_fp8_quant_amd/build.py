@@ -31,8 +31,19 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
+def _silu_table() -> None:
+    """Generate the exact bf16(silu) table the 1x128 SiLU kernel reads for
+    gates near a rounding midpoint (when missing or older than its
+    generator)."""
+    gen = os.path.join(CSRC, "gen_silu_table.py")
+    inc = os.path.join(CSRC, "silu_bf16_table.inc")
+    if not os.path.exists(inc) or os.path.getmtime(inc) < os.path.getmtime(gen):
+        _run([sys.executable, gen, inc])
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _silu_table()
     kobj = os.path.join(BUILD, "afq_kernels.o")
     aobj = os.path.join(BUILD, "afq_abi.o")
     _run([HIPCC, "-c", f"--offload-arch={ARCH}", *COMMON, *NO_PACKED_FP32,

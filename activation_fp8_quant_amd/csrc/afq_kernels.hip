@@ -300,49 +300,17 @@ __device__ __noinline__ float silu_f32_slow(float g)
 }
 
 
-// bf16 code of the two-term value hi + lo (lo a correction far below an
-// fp64 ulp of hi that only decides an exact midpoint of hi), sign given
-// separately; round to nearest even.
-__device__ __forceinline__ uint32_t bf16_of_double2(double hi, double lo, uint32_t sign)
-{
-    const double ad = __builtin_fabs(hi);
-    const double t = hi < 0.0 ? -lo : lo; // the tail, measured along |hi|
-    if (ad < 0x1p-126) {
-        // bf16 subnormals: a count of 2^-133 steps
-        const double k = ad * 0x1p133; // exact scaling
-        const double kf = __builtin_floor(k);
-        const double fr = k - kf;       // exact
-        uint32_t c = (uint32_t)kf;
-        if (fr > 0.5 || (fr == 0.5 && (t > 0.0 || (t == 0.0 && (c & 1u))))) ++c;
-        return sign | c;
-    }
-    // fp64 keeps 52 mantissa bits, bf16 7: drop 45 (a carry of the round-up
-    // moves into the exponent field), then rebias the exponent 1023 -> 127
-    const uint64_t db = (uint64_t)__double_as_longlong(ad);
-    const uint64_t rem = db & ((1ull << 45) - 1);
-    uint64_t base = db >> 45;
-    const uint64_t half = 1ull << 44;
-    if (rem > half || (rem == half && (t > 0.0 || (t == 0.0 && (base & 1ull))))) ++base;
-    return sign | (uint32_t)(base - ((uint64_t)(1023 - 127) << 7));
-}
+// bf16(silu(g)) of the 8 bf16 gates of a chunk (bits in gb), exactly
+// rounded, as fp32 values.  The fast fp32 value is within 2 ulp of silu(g)
+// for every bf16 gate >= -80 (measured over all of them), so its bf16
+// rounding is the exact one unless it sits within 3 fp32 ulps of a bf16
+// rounding midpoint; such gates, and gates below -80 (e^-g beyond the fp32
+// range), read the exact value from kSiluBf16Table (generated from the
+// definition in decimal arithmetic by gen_silu_table.py).  The common path
+// has no branch; a chunk holding a flagged gate takes one.
+#include "silu_bf16_table.inc"
 
-__device__ __noinline__ uint32_t silu_bf16_slow(float g)
-{
-    double hi, lo;
-    silu_f64(g, hi, lo);
-    // silu(g) = g * logistic(g) has the sign of g (also for -0 and for
-    // underflow to zero)
-    return bf16_of_double2(hi, lo, (__float_as_uint(g) >> 16) & 0x8000u);
-}
-
-// bf16(silu(g)) of 8 bf16 gates, exactly rounded, as fp32 values.  The
-// fast fp32 value is within 2 ulp of silu(g) for every bf16 gate >= -80
-// (measured over all of them), so its bf16 rounding is the exact one unless
-// it sits within 3 fp32 ulps of a bf16 rounding midpoint; such gates, and
-// gates below -80 (e^-g beyond the fp32 range), are redone in fp64.  The
-// common path has no branch; a chunk holding a flagged gate (rare) takes
-// one.
-__device__ __forceinline__ void silu_bf16x8(const float (&g)[8], float (&s)[8])
+__device__ __forceinline__ void silu_bf16x8(const float (&g)[8], const uint4 &gb, float (&s)[8])
 {
     float raw[8];
     uint32_t dmin = 0xFFFFFFFFu; // (low 16 bits) - (0x8000 - 3): <= 6 when within 3 ulps of a midpoint
@@ -355,10 +323,14 @@ __device__ __forceinline__ void silu_bf16x8(const float (&g)[8], float (&s)[8])
     }
     round8<kBF16>(s);
     if (__builtin_expect(dmin <= 6u || gmin < -80.0f, 0)) {
-#pragma unroll 1
-        for (int i = 0; i < 8; ++i)
-            if (g[i] < -80.0f || ((__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u)) <= 6u)
-                s[i] = __uint_as_float(silu_bf16_slow(g[i]) << 16);
+        const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (g[i] < -80.0f || ((__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u)) <= 6u) {
+                const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+                s[i] = __uint_as_float((uint32_t)kSiluBf16Table[bits] << 16);
+            }
+        }
     }
 }
 
@@ -420,7 +392,7 @@ act_quant_kernel(const ActArgs a)
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
         } else {
             float sg[8];
-            silu_bf16x8(g, sg);
+            silu_bf16x8(g, gv[k], sg);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] *= sg[i];
             const uint4 ap = round8<kBF16>(v);
