@@ -176,9 +176,16 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: torch.device) -> int:
+    """The HIP stream handle to enqueue on: the given stream, else torch's
+    current stream on the tensors' device."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is not None:
+            return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -269,7 +276,7 @@ def fused_add_rmsnorm_quant(
             residual_out = residual if inplace else torch.empty_like(residual)
         d.residual_in, d.residual_out = residual.data_ptr(), residual_out.data_ptr()
         results[0].residual = residual_out
-    st = lib.fused_add_rmsnorm_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    st = lib.fused_add_rmsnorm_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, xs[0].device)))
     if st != 0:
         raise AfqError(st, "fused_add_rmsnorm_quant")
     return results[0] if len(results) == 1 else results
@@ -297,7 +304,7 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
     d = _ActDesc()
     d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
-    st = lib.silu_mul_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    st = lib.silu_mul_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, gate_up.device)))
     if st != 0:
         raise AfqError(st, "silu_mul_quant")
     return QuantizedActivation(values, scales, act, None, mode, gate_up.dtype, (M, I))
@@ -316,7 +323,7 @@ def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> Quantize
     d.M, d.cols, d.x, d.x_row_stride = M, cols, x.data_ptr(), x.stride(0)
     d.dtype, d.mode = _DTYPE_TAG[x.dtype], mode
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), None
-    st = lib.fp8_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream)))
+    st = lib.fp8_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, x.device)))
     if st != 0:
         raise AfqError(st, "fp8_quant")
     return QuantizedActivation(values, scales, None, None, mode, x.dtype, (M, cols))

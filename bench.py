@@ -344,12 +344,14 @@ def main():
         for name, make, ws, m in big:
             k = rotation_sets(ws)
             c = make(k)
-            ms_c = time_events(c, 100, 10)
-            sweep.append({"workload": name, "M": m, "us_per_launch": round(ms_c * 1e3, 2),
-                          "GBps": round(c.bytes / ms_c / 1e6, 1),
-                          "pct_hbm_peak": round(100 * c.bytes / ms_c / 1e6 / HBM_PEAK_GBS, 1),
-                          "method": f"events over 100 launches, {k} rotating buffer sets"})
-            print(f"[bench] {name} M={m}: {ms_c * 1e3:.2f} us", file=sys.stderr, flush=True)
+            iters = max(2 * k, 20)
+            us_c = graph_time_us(c, iters=iters, reps=10)
+            sweep.append({"workload": name, "M": m, "us_per_launch": round(us_c, 2),
+                          "GBps": round(c.bytes / us_c / 1e3, 1),
+                          "pct_hbm_peak": round(100 * c.bytes / us_c / 1e3 / HBM_PEAK_GBS, 1),
+                          "method": f"graph replay of {iters} launches over {k} rotating buffer sets, "
+                                    "median of 10"})
+            print(f"[bench] {name} M={m}: {us_c:.2f} us", file=sys.stderr, flush=True)
             del c
             torch.cuda.empty_cache()
         result["sweep"] = sweep
