@@ -41,18 +41,33 @@ def _silu_table() -> None:
         _run([sys.executable, gen, inc])
 
 
+# one translation unit per kernel family
+KERNEL_SOURCES = ("afq_norm.hip", "afq_act.hip", "afq_quant.hip")
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     _silu_table()
-    kobj = os.path.join(BUILD, "afq_kernels.o")
-    aobj = os.path.join(BUILD, "afq_abi.o")
-    _run([HIPCC, "-c", f"--offload-arch={ARCH}", *COMMON, *NO_PACKED_FP32,
-          "-x", "hip", os.path.join(CSRC, "afq_kernels.hip"), "-o", kobj])
+    cmds, objs = [], []
+    for src in KERNEL_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        cmds.append([HIPCC, "-c", f"--offload-arch={ARCH}", *COMMON, *NO_PACKED_FP32,
+                     "-x", "hip", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
     # the ABI translation unit is plain host C++ (no HIP headers)
-    _run(["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
-          f"-I{INCLUDE}", f"-I{CSRC}", os.path.join(CSRC, "afq_abi.cpp"), "-o", aobj])
+    aobj = os.path.join(BUILD, "afq_abi.o")
+    cmds.append(["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+                 f"-I{INCLUDE}", f"-I{CSRC}", os.path.join(CSRC, "afq_abi.cpp"), "-o", aobj])
+    objs.append(aobj)
+    procs = []
+    for c in cmds:
+        print("+", " ".join(c), flush=True)
+        procs.append(subprocess.Popen(c))
+    bad = [c for c, p in zip(cmds, procs) if p.wait() != 0]
+    if bad:
+        raise subprocess.CalledProcessError(1, bad[0])
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -2,7 +2,8 @@
 //
 // Everything here runs on the host before any enqueue, touches no device
 // memory and makes no HIP call, so a rejected call has written nothing.
-// The launchers (afq_kernels.hip) are the only code that talks to HIP.
+// The launchers (afq_norm.hip, afq_act.hip, afq_quant.hip) are the only
+// code that talks to HIP.
 
 #include "afq.h"
 #include "afq_internal.h"

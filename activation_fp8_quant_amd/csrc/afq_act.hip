@@ -1,0 +1,212 @@
+// afq_act.hip -- SiLU-and-mul fused with FP8 quantisation.
+//
+// act_quant_kernel works on a flat chunk index (8 activations per chunk):
+// a row has no cross-row work, so every lane is busy for any width I.
+// HBM-bound elementwise work: no dense contraction, so no MFMA.
+
+#include "afq_device.hpp"
+#include "afq_internal.h"
+#include "afq_launch.hpp"
+
+namespace afq {
+
+struct ActArgs {
+    const uint8_t *gu;
+    int64_t gu_pitch;
+    uint8_t *values;
+    uint8_t *scales;
+    uint8_t *act;
+    uint32_t total;   // chunks of this launch (rows * C), < 2^32
+    int32_t C;        // chunks per row (I / 8)
+    int32_t I;
+    DivC dc;          // division by C
+};
+
+// silu(g) = g / (1 + e^-g) in fp32 for a bf16 gate g >= -80, within 2 ulp
+// of the fp64 value (measured over every such gate).  log2(e) is split as
+// kHi + kLo with a 16-bit head, so t = -g kHi is exact for a bf16 g and
+// e^-g = 2^t e^y with y = -g kLo ln 2 (|y| < 4e-4 for |g| <= 80); the
+// hardware exp2 gives 2^t and e^y is taken to first order.  For large
+// positive g, 2^t vanishes and y is clamped so that the product stays
+// finite.  Then g times the hardware reciprocal of 1 + e^-g.
+__device__ __forceinline__ float silu_fast(float g)
+{
+    constexpr float kHi = 1.44268798828125f;    // log2(e) to 16 significant bits
+    constexpr float kLoLn2 = 4.8884954e-06f;    // (log2(e) - kHi) ln 2
+    const float t = g * -kHi;
+    const float y = __builtin_fmaxf(g * -kLoLn2, -0.01f);
+    const float e0 = __builtin_amdgcn_exp2f(t);
+    const float e = __builtin_fmaf(e0, y, e0);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// silu in fp64 as a two-term value hi + lo: for |g| < 1/2 as g/2 + (g/2)
+// tanh(g/2) (for tiny g the plain quotient collapses to exactly g/2, a
+// possible rounding midpoint, and the second term keeps the g^2/4 that
+// decides it); else g e^g / (1 + e^g) (g < 0, no overflow) or
+// g / (1 + e^-g).  A zero gate returns itself (silu(-0) = -0).
+__device__ __forceinline__ void silu_f64(float g, double &hi, double &lo)
+{
+    const double gd = (double)g;
+    lo = 0.0;
+    if (gd == 0.0) {
+        hi = gd;
+    } else if (__builtin_fabs(gd) < 0.5) {
+        const double a = gd * 0.5, b = a * tanh(a);
+        hi = a + b;
+        lo = b - (hi - a);
+    } else if (gd < 0.0) {
+        const double e = exp(gd);
+        hi = gd * e / (1.0 + e);
+    } else {
+        hi = gd / (1.0 + exp(-gd));
+    }
+}
+
+__device__ __noinline__ float silu_f32_slow(float g)
+{
+    double hi, lo;
+    silu_f64(g, hi, lo);
+    return (float)(hi + lo);
+}
+
+
+// bf16(silu(g)) of the 8 bf16 gates of a chunk (bits in gb), exactly
+// rounded, as fp32 values.  The fast fp32 value is within 2 ulp of silu(g)
+// for every bf16 gate >= -80 (measured over all of them), so its bf16
+// rounding is the exact one unless it sits within 3 fp32 ulps of a bf16
+// rounding midpoint; such gates, and gates below -80 (e^-g beyond the fp32
+// range), read the exact value from kSiluBf16Table (generated from the
+// definition in decimal arithmetic by gen_silu_table.py).  The common path
+// has no branch; a chunk holding a flagged gate takes one.
+#include "silu_bf16_table.inc"
+
+__device__ __forceinline__ void silu_bf16x8(const float (&g)[8], const uint4 &gb, float (&s)[8])
+{
+    float raw[8];
+    uint32_t dmin = 0xFFFFFFFFu; // (low 16 bits) - (0x8000 - 3): <= 6 when within 3 ulps of a midpoint
+    float gmin = g[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        raw[i] = s[i] = silu_fast(g[i]);
+        dmin = min(dmin, (__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u));
+        gmin = __builtin_fminf(gmin, g[i]);
+    }
+    round8<kBF16>(s);
+    if (__builtin_expect(dmin <= 6u || gmin < -80.0f, 0)) {
+        const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (g[i] < -80.0f || ((__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u)) <= 6u) {
+                const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+                s[i] = __uint_as_float((uint32_t)kSiluBf16Table[bits] << 16);
+            }
+        }
+    }
+}
+
+// fp32 silu of 8 gates for the MXFP8 path: the fast form; gates below -80
+// (e^-g beyond the fp32 range) are redone in fp64.
+__device__ __forceinline__ void silu_f32x8(const float (&g)[8], float (&s)[8])
+{
+    float gmin = g[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] = silu_fast(g[i]);
+        gmin = __builtin_fminf(gmin, g[i]);
+    }
+    if (gmin < -80.0f) {
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i)
+            if (g[i] < -80.0f) s[i] = silu_f32_slow(g[i]);
+    }
+}
+
+template <int MODE, int CPL>
+__global__ void __launch_bounds__(256)
+act_quant_kernel(const ActArgs a)
+{
+    const uint32_t base = blockIdx.x * (256u * CPL) + threadIdx.x;
+    uint4 gv[CPL], uv[CPL];
+    bool ok[CPL];
+    int64_t rw[CPL];
+    int32_t lc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const uint32_t f = base + k * 256u;
+        ok[k] = f < a.total;
+        const uint32_t r = div_c(f, a.dc);
+        rw[k] = r;
+        lc[k] = (int32_t)(f - r * (uint32_t)a.C);
+        if (ok[k]) {
+            const uint8_t *p = a.gu + rw[k] * a.gu_pitch + (int64_t)lc[k] * 16;
+            gv[k] = ldg_stream(p);
+            uv[k] = ldg_stream(p + (int64_t)a.I * 2);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        if (!ok[k]) continue; // uniform over every quant group
+        float g[8], v[8];
+        unpack8<kBF16>(gv[k], g);
+        unpack8<kBF16>(uv[k], v);
+        const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
+        uint2 q;
+        if constexpr (MODE == kMX) {
+            float sg[8];
+            silu_f32x8(g, sg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+            if (a.act) stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
+            const uint32_t b = e8m0_of(max_quad(amax8(v)));
+            q = mx_codes8(v, mx_inv_scale(b));
+            if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
+        } else {
+            float sg[8];
+            silu_bf16x8(g, gv[k], sg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+            const uint4 ap = round8<kBF16>(v);
+            if (a.act) stg_stream(a.act + out_off * 2, ap);
+            const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
+            q = fp32scale_codes8(v, sc);
+            if ((lc[k] & 15) == 0)
+                reinterpret_cast<float *>(a.scales)[rw[k] * (a.I / 128) + lc[k] / 16] = sc.s;
+        }
+        stg_stream(a.values + out_off, q);
+    }
+}
+
+// ================================================================ launcher
+template <int MODE, int CPL>
+static hipError_t go_act(const ActArgs &a, hipStream_t st)
+{
+    const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+int launch_act(const ActPlan &p, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t C = p.I / 8;
+    const int64_t step = flat_rows_per_launch(C);
+    for (int64_t r0 = 0; r0 < p.M; r0 += step) {
+        const int64_t rows = p.M - r0 < step ? p.M - r0 : step;
+        ActArgs a;
+        a.gu = p.gu + r0 * p.gu_pitch;
+        a.gu_pitch = p.gu_pitch;
+        a.values = p.values + r0 * p.I;
+        a.scales = p.scales + r0 * (p.mode == kMX ? p.I / 32 : 4 * (p.I / 128));
+        a.act = p.act ? p.act + r0 * p.I * 2 : nullptr;
+        a.C = C;
+        a.I = p.I;
+        a.total = (uint32_t)(rows * C);
+        a.dc = divc((uint32_t)C);
+        hipError_t e = p.mode == kMX ? go_act<kMX, 1>(a, st) : go_act<kB128, 1>(a, st);
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
+}
+
+} // namespace afq

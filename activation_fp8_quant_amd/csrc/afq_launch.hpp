@@ -1,0 +1,63 @@
+// afq_launch.hpp -- launch-shape helpers shared by the kernel launchers:
+// the row shape of the row kernels, the rows per launch of the flat
+// kernels, and the flat kernels' division of a chunk index by the chunks
+// per row (multiplier made on the host, applied on the device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace afq {
+
+// Division of a flat 32-bit chunk index by the chunks per row C, by a
+// multiplier computed on the host (round-up method): with l = ceil(log2 C)
+// and m = floor(2^32 (2^l - C) / C) + 1, n / C = (mulhi(n, m) + n) >> l
+// for every n < 2^32 (the sum is taken in 64 bits).
+struct DivC {
+    uint32_t m;
+    uint32_t l;
+};
+static inline DivC divc(uint32_t C)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < C) ++l;
+    DivC d;
+    d.m = (uint32_t)(((1ull << 32) * ((1ull << l) - C)) / C + 1);
+    d.l = l;
+    return d;
+}
+__device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
+{
+    return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
+}
+
+// Row shape for a row of C chunks.  Few rows (latency-bound: every lane of
+// a row works through its chunks one after the other, so the row's time
+// grows with the chunks per lane): as many lanes as chunks, up to 1024.
+// Many rows (bandwidth-bound): two chunks per lane, which measured best or
+// within a few % of best on every configured width (hidden 6144 MX + copy,
+// 4096 1x128, the 1536 + 512 two-segment per-token rows).  NT is a whole
+// number of wavefronts; rows of fewer than 256 lanes are packed several to
+// a block.
+struct RowShapeRt {
+    int NT, CPL, R, WPR;
+};
+static inline RowShapeRt row_shape(int C, int64_t M)
+{
+    RowShapeRt s;
+    int cpl = M <= 1024 ? 1 : 2;
+    if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
+    int nt = (C + cpl - 1) / cpl;
+    nt = (nt + 63) / 64 * 64;
+    s.NT = nt;
+    s.CPL = (C + nt - 1) / nt;
+    s.R = (nt < 256 && 256 % nt == 0) ? 256 / nt : 1;
+    s.WPR = nt / 64;
+    return s;
+}
+
+// Rows per launch of the flat kernels: the flat chunk index stays below
+// 2^31 (larger M is covered by several launches over row slices).
+static inline int64_t flat_rows_per_launch(int32_t C) { return ((int64_t)1 << 31) / C; }
+
+} // namespace afq

@@ -1,0 +1,279 @@
+// afq_norm.hip -- residual add + RMSNorm fused with FP8 quantisation.
+//
+// norm_quant_kernel: one row (one or two segments) per NT lanes; residual
+// add, fp32 sum of squares (DPP inside a wavefront, one LDS step across
+// wavefronts), scale by the weight, round to the activation dtype,
+// quantise.  HBM-bound row work: no dense contraction, so no MFMA.
+//
+// Every lane issues all of its 16-byte loads before it does any arithmetic,
+// so a row's whole input is in flight at once; stores are 16 B (dtype
+// outputs) and 8 B (codes) per lane, contiguous across the wavefront.
+
+#include "afq_device.hpp"
+#include "afq_internal.h"
+#include "afq_launch.hpp"
+
+namespace afq {
+
+// Rows are NT lanes (a whole number of wavefronts, NT <= 1024); a block
+// holds R rows (R > 1 only for NT of 64 or 128 lanes).  Both are launch
+// parameters; the per-lane chunk count CPL and the segment count NSEG are
+// template parameters (the loops over a lane's chunks are unrolled, and a
+// single-segment row carries no segment selection).
+constexpr int kMaxBlock = 1024;
+
+struct NormArgs {
+    NormSegPlan seg[2];
+    const uint8_t *res_in;
+    uint8_t *res_out;
+    int64_t M;
+    float eps;
+    int32_t C0;        // chunks of segment 0
+    int32_t C;         // chunks of both segments
+    int32_t NT;        // lanes per row
+    int32_t R;         // rows per block
+    int32_t WPR;       // wavefronts per row
+    int32_t wpr_shift; // log2(WPR) when R > 1
+    float inv_cols0;   // 1 / cols of each segment (the mean of the squares)
+    float inv_cols1;
+};
+
+// sum of squares of the 8 values of a packed chunk (v_dot2 on pairs)
+template <int DT>
+__device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
+{
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (DT == kBF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
+                                                  __builtin_bit_cast(bf16x2, w[i]), acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]),
+                                         __builtin_bit_cast(f16x2, w[i]), acc, false);
+    }
+    return acc;
+}
+
+template <int DT, int MODE, bool GEMMA, int CPL, int NSEG>
+__global__ void __launch_bounds__(kMaxBlock)
+norm_quant_kernel(const NormArgs a)
+{
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
+    const int t = tid - rib * a.NT;                       // lane within the row
+    const int64_t row = (int64_t)blockIdx.x * a.R + rib;
+    const bool row_ok = row < a.M;
+    const bool has_res = a.res_in != nullptr;
+
+    // per-row bases
+    const uint8_t *xrow0 = a.seg[0].x + row * a.seg[0].x_pitch;
+    const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + row * a.seg[1].x_pitch : xrow0;
+    const int64_t rrow = row * a.C0 * 16;
+
+    // ---- issue every load of the row
+    uint4 xv[CPL], rv[CPL], wv[CPL];
+    bool ok[CPL];
+    int sg[CPL], lc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = t + k * a.NT;
+        ok[k] = row_ok && c < a.C;
+        if constexpr (NSEG == 1) {
+            sg[k] = 0;
+            lc[k] = c;
+        } else {
+            sg[k] = c >= a.C0 ? 1 : 0;
+            lc[k] = c - (sg[k] ? a.C0 : 0);
+        }
+        if (ok[k]) {
+            xv[k] = ldg_stream((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
+            wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
+            if (has_res)
+                rv[k] = ldg_stream(a.res_in + rrow + lc[k] * 16);
+        }
+    }
+
+    // ---- residual add (h = round_dt(x + r), stored), sum of squares
+    float h[CPL][8];
+    float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        if (!ok[k]) continue;
+        uint4 hp = xv[k];
+        if (has_res) {
+            float rf[8];
+            unpack8<DT>(xv[k], h[k]);
+            unpack8<DT>(rv[k], rf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
+            hp = pack8<DT>(h[k]);
+            stg_stream(a.res_out + rrow + lc[k] * 16, hp);
+        }
+        unpack8<DT>(hp, h[k]);
+        if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
+        else ss0 = sumsq8<DT>(hp, ss0);
+    }
+
+    // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
+    //      across the wavefronts of the row
+    __shared__ float red[kMaxBlock / 64][2];
+    __shared__ float redm[kMaxBlock / 64][2];
+    ss0 = sum_wave(ss0);
+    if constexpr (NSEG > 1) ss1 = sum_wave(ss1);
+    if (a.WPR > 1) {
+        if ((tid & 63) == 0) {
+            red[wave][0] = ss0;
+            if constexpr (NSEG > 1) red[wave][1] = ss1;
+        }
+        lds_barrier();
+        ss0 = 0.f;
+        ss1 = 0.f;
+        for (int i = 0; i < a.WPR; ++i) {
+            ss0 += red[rib * a.WPR + i][0];
+            if constexpr (NSEG > 1) ss1 += red[rib * a.WPR + i][1];
+        }
+    }
+    const float inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
+    const float inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
+
+    // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
+    //      Gemma: g * inv = (1 + w) inv as one FMA.
+    float am0 = 0.f, am1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        if (!ok[k]) continue;
+        const float inv = sg[k] ? inv1 : inv0;
+        float wf[8];
+        unpack8<DT>(wv[k], wf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
+        const uint4 up = round8<DT>(h[k]);
+        uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
+        const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
+        if (normed)
+            stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
+        if constexpr (MODE == kPT) {
+            const float m = amax8(h[k]);
+            if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
+        }
+    }
+
+    // ---- quantise
+    if constexpr (MODE == kPT) {
+        am0 = max_wave(am0);
+        if constexpr (NSEG > 1) am1 = max_wave(am1);
+        if (a.WPR > 1) {
+            if ((tid & 63) == 0) {
+                redm[wave][0] = am0;
+                if constexpr (NSEG > 1) redm[wave][1] = am1;
+            }
+            lds_barrier();
+            am0 = 0.f;
+            am1 = 0.f;
+            for (int i = 0; i < a.WPR; ++i) {
+                am0 = __builtin_fmaxf(am0, redm[rib * a.WPR + i][0]);
+                if constexpr (NSEG > 1) am1 = __builtin_fmaxf(am1, redm[rib * a.WPR + i][1]);
+            }
+        }
+        const Fp32Scale sc0 = fp32_scale(am0);
+        const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k]) continue;
+            const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+            const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
+            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+            if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k]) continue; // uniform over every quant group
+            const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+            uint2 q;
+            if constexpr (MODE == kMX) {
+                const uint32_t b = e8m0_of(max_quad(amax8(h[k])));
+                q = mx_codes8(h[k], mx_inv_scale(b));
+                if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b;
+            } else {
+                const Fp32Scale sc = fp32_scale(max_row16(amax8(h[k])));
+                q = fp32scale_codes8(h[k], sc);
+                if ((lc[k] & 15) == 0)
+                    reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
+            }
+            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+        }
+    }
+}
+
+// ================================================================ launcher
+template <int DT, int MODE, bool GEMMA, int CPL>
+static hipError_t go_norm(const NormArgs &a, int nseg, hipStream_t st)
+{
+    const int64_t blocks = (a.M + a.R - 1) / a.R;
+    if (nseg > 1)
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2>), dim3((unsigned)blocks),
+                           dim3(a.NT * a.R), 0, st, a);
+    else
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1>), dim3((unsigned)blocks),
+                           dim3(a.NT * a.R), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int MODE, bool GEMMA>
+static hipError_t go_norm_cpl(const NormArgs &a, int nseg, int CPL, hipStream_t st)
+{
+    switch (CPL) {
+    case 1: return go_norm<DT, MODE, GEMMA, 1>(a, nseg, st);
+    case 2: return go_norm<DT, MODE, GEMMA, 2>(a, nseg, st);
+    case 3: return go_norm<DT, MODE, GEMMA, 3>(a, nseg, st);
+    default: return go_norm<DT, MODE, GEMMA, 4>(a, nseg, st);
+    }
+}
+
+template <int DT, int MODE>
+static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int nseg, int CPL, hipStream_t st)
+{
+    return gemma ? go_norm_cpl<DT, MODE, true>(a, nseg, CPL, st)
+                 : go_norm_cpl<DT, MODE, false>(a, nseg, CPL, st);
+}
+
+template <int DT>
+static hipError_t go_norm_mode(const NormArgs &a, int mode, bool gemma, int nseg, int CPL, hipStream_t st)
+{
+    switch (mode) {
+    case kMX: return go_norm_kind<DT, kMX>(a, gemma, nseg, CPL, st);
+    case kB128: return go_norm_kind<DT, kB128>(a, gemma, nseg, CPL, st);
+    default: return go_norm_kind<DT, kPT>(a, gemma, nseg, CPL, st);
+    }
+}
+
+int launch_norm(const NormPlan &p, void *stream)
+{
+    NormArgs a;
+    a.seg[0] = p.seg[0];
+    a.seg[1] = p.nseg > 1 ? p.seg[1] : p.seg[0];
+    a.res_in = p.res_in;
+    a.res_out = p.res_out;
+    a.M = p.M;
+    a.eps = p.eps;
+    a.C0 = p.seg[0].chunks;
+    a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
+    const RowShapeRt sh = row_shape(a.C, p.M);
+    a.NT = sh.NT;
+    a.R = sh.R;
+    a.WPR = sh.WPR;
+    a.wpr_shift = sh.WPR == 2 ? 1 : 0; // R > 1 only with one or two wavefronts per row
+    a.inv_cols0 = 1.0f / (float)p.seg[0].cols;
+    a.inv_cols1 = 1.0f / (float)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
+    hipStream_t st = (hipStream_t)stream;
+    const bool gemma = p.kind == 1;
+    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, p.nseg, sh.CPL, st)
+                                    : go_norm_mode<kBF16>(a, p.mode, gemma, p.nseg, sh.CPL, st);
+    return (int)e;
+}
+
+} // namespace afq
