@@ -26,18 +26,17 @@ struct ActArgs {
 // of the fp64 value (measured over every such gate).  log2(e) is split as
 // kHi + kLo with a 16-bit head, so t = -g kHi is exact for a bf16 g and
 // e^-g = 2^t e^y with y = -g kLo ln 2 (|y| < 4e-4 for |g| <= 80); the
-// hardware exp2 gives 2^t and e^y is taken to first order.  For large
-// positive g, 2^t vanishes and y is clamped so that the product stays
-// finite.  Then g times the hardware reciprocal of 1 + e^-g.
+// hardware exp2 gives 2^t and e^y is taken to first order, so that
+// 1 + e^-g = 2^t (1 + y) + 1 is two FMAs.  For large positive g, 2^t is
+// zero and the denominator is 1.  Then g times the hardware reciprocal.
 __device__ __forceinline__ float silu_fast(float g)
 {
     constexpr float kHi = 1.44268798828125f;    // log2(e) to 16 significant bits
     constexpr float kLoLn2 = 4.8884954e-06f;    // (log2(e) - kHi) ln 2
     const float t = g * -kHi;
-    const float y = __builtin_fmaxf(g * -kLoLn2, -0.01f);
-    const float e0 = __builtin_amdgcn_exp2f(t);
-    const float e = __builtin_fmaf(e0, y, e0);
-    return g * __builtin_amdgcn_rcpf(1.0f + e);
+    const float w = __builtin_fmaf(g, -kLoLn2, 1.0f);
+    const float d = __builtin_fmaf(__builtin_amdgcn_exp2f(t), w, 1.0f);
+    return g * __builtin_amdgcn_rcpf(d);
 }
 
 // silu in fp64 as a two-term value hi + lo: for |g| < 1/2 as g/2 + (g/2)
@@ -122,6 +121,25 @@ __device__ __forceinline__ void silu_f32x8(const float (&g)[8], float (&s)[8])
     }
 }
 
+// The 1x128 outputs of one chunk from s = bf16(silu(gate)) and the up
+// values v (fp32, overwritten): a = bf16(s * up), the group scale
+// amax|a| / 448 over the 16 lanes of the group, the codes, and the
+// optional bf16 copy of a.
+__device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8], float (&v)[8],
+                                          int64_t r, int32_t lc)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= s[i];
+    const uint4 ap = round8<kBF16>(v);
+    const int64_t out_off = r * a.I + (int64_t)lc * 8;
+    if (a.act) stg_stream(a.act + out_off * 2, ap);
+    const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
+    const uint2 q = fp32scale_codes8(v, sc);
+    if ((lc & 15) == 0)
+        reinterpret_cast<float *>(a.scales)[r * (a.I / 128) + lc / 16] = sc.s;
+    stg_stream(a.values + out_off, q);
+}
+
 template <int MODE, int CPL>
 __global__ void __launch_bounds__(256)
 act_quant_kernel(const ActArgs a)
@@ -150,9 +168,9 @@ act_quant_kernel(const ActArgs a)
         float g[8], v[8];
         unpack8<kBF16>(gv[k], g);
         unpack8<kBF16>(uv[k], v);
-        const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
-        uint2 q;
         if constexpr (MODE == kMX) {
+            const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
+            uint2 q;
             float sg[8];
             silu_f32x8(g, sg);
 #pragma unroll
@@ -161,19 +179,12 @@ act_quant_kernel(const ActArgs a)
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
+            stg_stream(a.values + out_off, q);
         } else {
             float sg[8];
             silu_bf16x8(g, gv[k], sg);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
-            const uint4 ap = round8<kBF16>(v);
-            if (a.act) stg_stream(a.act + out_off * 2, ap);
-            const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
-            q = fp32scale_codes8(v, sc);
-            if ((lc[k] & 15) == 0)
-                reinterpret_cast<float *>(a.scales)[rw[k] * (a.I / 128) + lc[k] / 16] = sc.s;
+            b128_tail(a, sg, v, rw[k], lc[k]);
         }
-        stg_stream(a.values + out_off, q);
     }
 }
 

@@ -268,31 +268,38 @@ __device__ __forceinline__ Fp32Scale fp32_scale(float amax)
     return sc;
 }
 
-// fp32(u / s), correctly rounded.  With r = RN(1/s), q0 = RN(u r) is within
-// one ulp of u/s, the remainder u - q0 s is exact under FMA, and one
-// correction step q0 + rem * r rounds to the correctly rounded quotient
-// (Markstein's theorem; no overflow since |u/s| <= 448(1+2^-23)).  Scales
-// that are subnormal or whose reciprocal overflows take the IEEE division.
-// The sign is copied from u so that u = -0 gives -0.
-__device__ __forceinline__ float quotient(float u, const Fp32Scale &sc)
+// fp32(u / s), correctly rounded, for a scale with sc.fast set.  With
+// r = RN(1/s), q0 = RN(u r) is within one ulp of u/s, so the remainder
+// q0 s - u is exact under FMA, and one correction step q0 - (q0 s - u) r
+// rounds to the correctly rounded quotient (Markstein's theorem; no
+// overflow since |u/s| <= 448(1+2^-23)).  Taking the remainder as q0 s - u
+// keeps the sign of a zero u (-0 gives -0): for u = -0 the correction is
+// -(+0) r + (-0) = -0.
+__device__ __forceinline__ float quotient_fast(float u, const Fp32Scale &sc)
 {
-    float q;
-    if (sc.fast) {
-        const float q0 = u * sc.r;
-        const float rem = __builtin_fmaf(-q0, sc.s, u);
-        q = __builtin_fmaf(rem, sc.r, q0);
-    } else {
-        q = u / sc.s;
-    }
-    return __builtin_copysignf(q, u);
+    const float q0 = u * sc.r;
+    const float nrem = __builtin_fmaf(q0, sc.s, -u);
+    return __builtin_fmaf(-nrem, sc.r, q0);
 }
 
+// 8 codes of a chunk under an fp32 scale.  With a fast scale the quotients
+// are at most 448(1+2^-23) in magnitude, which v_cvt_pk_fp8_f32 rounds to
+// 448 exactly as it rounds the clamped value (checked on the GPU over every
+// fp32 in [448, 464] of either sign), so no clamp is applied.  Scales that
+// are subnormal or whose reciprocal overflows (amax below 448 * 2^-126) take
+// the IEEE division and the clamp.  The choice is made once per chunk (it is
+// uniform over a group).
 __device__ __forceinline__ uint2 fp32scale_codes8(const float (&u)[8], const Fp32Scale &sc)
 {
-    if (sc.zero) return make_uint2(0u, 0u);
     float v[8];
+    if (__builtin_expect(sc.fast, 1)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = clamp448(quotient(u[i], sc));
+        for (int i = 0; i < 8; ++i) v[i] = quotient_fast(u[i], sc);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = clamp448(__builtin_copysignf(u[i] / sc.s, u[i]));
+    }
+    if (sc.zero) return make_uint2(0u, 0u);
     return cvt8_e4m3(v);
 }
 

@@ -31,21 +31,23 @@ __device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
     return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
 }
 
-// Row shape for a row of C chunks.  Few rows (latency-bound: every lane of
-// a row works through its chunks one after the other, so the row's time
-// grows with the chunks per lane): as many lanes as chunks, up to 1024.
-// Many rows (bandwidth-bound): two chunks per lane, which measured best or
-// within a few % of best on every configured width (hidden 6144 MX + copy,
-// 4096 1x128, the 1536 + 512 two-segment per-token rows).  NT is a whole
-// number of wavefronts; rows of fewer than 256 lanes are packed several to
-// a block.
+// Row shape for a row of C chunks: one chunk per lane (as many lanes as
+// chunks, up to 1024), so that a row's loads are all in flight at once and
+// the per-lane work is shortest.  Per-token rows of a bandwidth-bound
+// launch (M > 1024) take two chunks per lane instead: they need two row
+// reductions (sum of squares, then amax), each an LDS exchange across the
+// row's wavefronts, and halving the wavefronts per row pays for the longer
+// lane work (measured at M = 8192, H = 2048..8192: per-token 4-14% faster
+// at two chunks; MXFP8 1-3% and 1x128 within 1% faster at one).  NT is a
+// whole number of wavefronts; rows of fewer than 256 lanes are packed
+// several to a block.
 struct RowShapeRt {
     int NT, CPL, R, WPR;
 };
-static inline RowShapeRt row_shape(int C, int64_t M)
+static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
 {
     RowShapeRt s;
-    int cpl = M <= 1024 ? 1 : 2;
+    int cpl = (per_token && M > 1024) ? 2 : 1;
     if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
     int nt = (C + cpl - 1) / cpl;
     nt = (nt + 63) / 64 * 64;

@@ -262,7 +262,7 @@ int launch_norm(const NormPlan &p, void *stream)
     a.eps = p.eps;
     a.C0 = p.seg[0].chunks;
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
-    const RowShapeRt sh = row_shape(a.C, p.M);
+    const RowShapeRt sh = row_shape(a.C, p.M, p.mode == kPT);
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;

@@ -5,15 +5,18 @@ Headline (the JSON `value`): fused add + Gemma RMSNorm + MXFP8 + bf16 copy,
 H = 6144, M = 16384 rows (the bandwidth-bound prefill shape), as achieved
 algorithmic HBM GB/s.  A step is one launch of that kernel over the batch;
 inputs are resident in HBM before timing starts.  Timing: W untimed
-launches, then K launches bracketed by HIP events on the launch stream (and
-a device synchronisation on both sides).
+launches (default 1000, about 150 ms: after an idle phase the GPU's clocks
+take some tens of ms of sustained work to settle), then K launches
+bracketed by HIP events on the launch stream (and a device synchronisation
+on both sides).
 
 Also reported, in the same JSON line:
   sweep        us/launch at decode sizes M = 8..192 by the graph-replay
-               method (200 launches captured in a HIP graph, 3 warm replays,
-               median of 20 timed replays / 200) for the fused norm and the
-               SiLU-and-mul + MXFP8 kernel, next to the figures the pages
-               print for their own kernels (context only); and the other
+               method (200 launches captured in a HIP graph, at least 200 ms
+               of untimed replays, then the median of 20 timed replays / 200)
+               for the fused norm and the SiLU-and-mul + MXFP8 kernel, next
+               to the figures the pages print for their own kernels
+               (context only); and the other
                workloads (1x128 norm / SiLU, per-token two-segment norm)
                timed with buffer rotation so that no launch reads data
                another launch left in the 256 MB last-level cache.
@@ -100,9 +103,11 @@ def time_events(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def graph_time_us(fn, iters=200, reps=20):
-    """us per launch by graph replay: capture `iters` launches, 3 warm
-    replays, median of `reps` timed replays divided by `iters`."""
+def graph_time_us(fn, iters=200, reps=20, warm_s=0.2):
+    """us per launch by graph replay: capture `iters` launches, replay for
+    at least `warm_s` seconds untimed (the GPU's clocks take some tens of ms
+    of sustained work to settle after an idle phase such as building the
+    inputs), then the median of `reps` timed replays divided by `iters`."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -114,8 +119,13 @@ def graph_time_us(fn, iters=200, reps=20):
             for _ in range(iters):
                 fn()
     torch.cuda.current_stream().wait_stream(st)
-    for _ in range(3):
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
         g.replay()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
@@ -248,7 +258,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -321,10 +331,10 @@ def main():
             us_s = graph_time_us(s)
             sweep.append({"workload": "norm gemma mx+copy H=6144", "M": m, "us_per_launch": round(us, 2),
                           "GBps": round(c.bytes / us / 1e3, 1), "page_us": PAGE_NORM_US[m],
-                          "method": "graph replay 200x, median of 20"})
+                          "method": "graph replay 200x after >= 200 ms warm replays, median of 20"})
             sweep.append({"workload": "silu-mul mx I=768", "M": m, "us_per_launch": round(us_s, 2),
                           "GBps": round(s.bytes / us_s / 1e3, 1), "page_us_swiglu_oai": PAGE_SWIGLU_US[m],
-                          "method": "graph replay 200x, median of 20"})
+                          "method": "graph replay 200x after >= 200 ms warm replays, median of 20"})
             print(f"[bench] M={m}: norm {us:.2f} us, silu {us_s:.2f} us", file=sys.stderr, flush=True)
             del c, s
         big = [
@@ -349,7 +359,8 @@ def main():
             sweep.append({"workload": name, "M": m, "us_per_launch": round(us_c, 2),
                           "GBps": round(c.bytes / us_c / 1e3, 1),
                           "pct_hbm_peak": round(100 * c.bytes / us_c / 1e3 / HBM_PEAK_GBS, 1),
-                          "method": f"graph replay of {iters} launches over {k} rotating buffer sets, "
+                          "method": f"graph replay of {iters} launches over {k} rotating buffer sets "
+                                    "after >= 200 ms warm replays, "
                                     "median of 10"})
             print(f"[bench] {name} M={m}: {us_c:.2f} us", file=sys.stderr, flush=True)
             del c

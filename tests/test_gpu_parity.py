@@ -111,6 +111,41 @@ def test_two_segment_per_token(dtype, M):
         _report(f"two-seg {dtype} M={M} cols={s['x'].shape[1]}", check_norm(gpu, ref, "pt", dtype, "two-seg"))
 
 
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+@pytest.mark.parametrize("H", [4096, 6144])
+def test_norm_bandwidth_row_counts(mode, H):
+    """Above 1024 rows a launch takes the bandwidth-bound row shape (two
+    chunks per lane for per-token rows): every row against the oracle."""
+    M = 1100
+    d = inputs.norm_inputs(M, H, seed=8, x_std=2.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
+    _report(f"bandwidth rows {mode} H={H}", check_norm(gpu, ref, mode, "bf16", f"bw-{mode}"))
+
+
+@pytest.mark.parametrize("M,sampled", [(2048, False), (8192, True)])
+def test_two_segment_bandwidth_row_counts(M, sampled):
+    """The two-segment per-token launch above 1024 rows (M = 8192 is the
+    benchmark workload, checked on sampled rows)."""
+    segs = inputs.two_segment_inputs(M, (1536, 512), seed=0)
+    buf = np.zeros((M, 2112), np.uint16)
+    buf[:, :1536] = segs[0]["x"]
+    buf[:, 1536:2048] = segs[1]["x"]
+    bt = dev16(buf)
+    outs = afq.fused_add_rmsnorm_quant([bt[:, :1536], bt[:, 1536:2048]],
+                                       [dev16(segs[0]["w"]), dev16(segs[1]["w"])], 1e-6,
+                                       mode=afq.PER_TOKEN, kind=afq.STANDARD, want_normed=True)
+    torch.cuda.synchronize()
+    rows = (np.sort(np.random.default_rng(1).choice(M, 64, replace=False)) if sampled
+            else np.arange(M))
+    for s, qa in zip(segs, outs):
+        gpu = dict(normed=host16(qa.normed)[rows], values=host8(qa.values)[rows],
+                   scales=scales_u8_or_f32(qa.scales)[rows])
+        ref = ref_norm(s["x"][rows], s["w"], kind="standard", mode="pt")
+        _report(f"two-seg bandwidth M={M} cols={s['x'].shape[1]}",
+                check_norm(gpu, ref, "pt", "bf16", "two-seg-bw"))
+
+
 def test_two_segment_other_modes():
     segs = inputs.two_segment_inputs(12, (1536, 512), seed=2)
     for mode in ("mx", "b128"):
@@ -167,6 +202,57 @@ def test_silu_b128_all_gates_exact():
     bad = np.flatnonzero(gpu["act"].ravel() != ref["act"].ravel())
     assert bad.size == 0, [hex(int(gu.reshape(-1, 256)[i // 128, i % 128])) for i in bad[:10]]
     assert np.array_equal(gpu["values"], ref["values"])
+
+
+# Launches of at least this many chunks (8 activations each) are the
+# bandwidth-bound prefill sizes; their rows must equal the same rows run as
+# a small launch (batch invariance) as well as the oracle.
+_LARGE_CHUNKS = 1 << 20
+
+
+def _silu_rows_small(gu, rows, mode):
+    """The given rows of gate_up run as their own (small) launch."""
+    return _run_silu(np.ascontiguousarray(gu[rows]), mode)
+
+
+@pytest.mark.parametrize("I,M,seed,std", [(12288, 4096, 0, 1.0),    # benchmark workloads
+                                          (3072, 16384, 1, 3.0),
+                                          (2176, 3900, 5, 2.0)])     # ragged last step
+def test_silu_b128_large_launch_sampled_rows(I, M, seed, std):
+    assert M * I // 8 >= _LARGE_CHUNKS
+    gu = inputs.gate_up_inputs(M, I, seed=seed, std=std)
+    gpu = _run_silu(gu, "b128")
+    rows = np.sort(np.random.default_rng(seed).choice(M, 48, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    ref = orc.silu_quant(gu, orc.BLOCK128, threads=8, rows=rows)
+    check_dtype16(gpu["act"][rows], ref["act"][rows], "silu-b128-large act", exact=True)
+    assert np.array_equal(gpu["values"][rows], ref["values"][rows])
+    assert np.array_equal(gpu["scales"][rows].view(np.uint32), ref["scales"][rows].view(np.uint32))
+    small = _silu_rows_small(gu, rows, "b128")
+    for k in ("act", "values", "scales"):
+        assert np.array_equal(gpu[k][rows].view(np.uint8), small[k].view(np.uint8)), k
+
+
+def test_silu_b128_large_launch_all_gates():
+    """Every finite bf16 gate (up = 1), tiled into a prefill-sized launch:
+    bit-identical to the oracle in every tile."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    gates = c[((c >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    pad = (-gates.size) % 128
+    g = np.concatenate([gates, np.zeros(pad, np.uint16)]).reshape(-1, 128)
+    one = inputs.to_bits(np.ones(1))[0]
+    block = np.concatenate([g, np.full_like(g, one)], axis=1)
+    reps = -(-_LARGE_CHUNKS // (block.shape[0] * 16))
+    gu = np.tile(block, (reps, 1))
+    assert gu.shape[0] * 16 >= _LARGE_CHUNKS
+    gpu = _run_silu(gu, "b128")
+    ref = orc.silu_quant(block, orc.BLOCK128, threads=8)
+    n = block.shape[0]
+    for r in range(reps):
+        sl = slice(r * n, (r + 1) * n)
+        assert np.array_equal(gpu["act"][sl], ref["act"]), r
+        assert np.array_equal(gpu["values"][sl], ref["values"]), r
+        assert np.array_equal(gpu["scales"][sl].view(np.uint32), ref["scales"].view(np.uint32)), r
 
 
 def test_silu_mx_extreme_gates():
