@@ -316,7 +316,7 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "norm_quant_kernel<bf16, MXFP8, Gemma, 2 chunks/lane, 1 segment>, 384 lanes per row"},
+                     "kernel": "norm_quant_kernel<bf16, MXFP8, Gemma, 1 chunk/lane, 1 segment>, 768 lanes per row"},
     }
     del head
     torch.cuda.empty_cache()
