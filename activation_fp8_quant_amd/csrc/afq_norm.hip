@@ -55,14 +55,22 @@ __device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
     return acc;
 }
 
-template <int DT, int MODE, bool GEMMA, int CPL, int NSEG>
+// SEGU (two segments only): the first segment's chunk count C0 is a
+// multiple of 64, so the chunks of slot k of a wavefront (64 consecutive
+// chunks starting at a multiple of 64) all lie in one segment; the segment
+// of each slot is then known per wavefront (scalar registers), and a
+// wavefront skips the reductions of a segment it holds no chunk of.
+template <int DT, int MODE, bool GEMMA, int CPL, int NSEG, bool SEGU>
 __global__ void __launch_bounds__(kMaxBlock)
 norm_quant_kernel(const NormArgs a)
 {
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // rows are whole wavefronts: the wavefront, its row and everything
+    // derived from them are wavefront-uniform (kept in scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
     const int t = tid - rib * a.NT;                       // lane within the row
+    const int tw = wave * 64 - rib * a.NT;                // t of the wavefront's lane 0
     const int64_t row = (int64_t)blockIdx.x * a.R + rib;
     const bool row_ok = row < a.M;
     const bool has_res = a.res_in != nullptr;
@@ -84,7 +92,7 @@ norm_quant_kernel(const NormArgs a)
             sg[k] = 0;
             lc[k] = c;
         } else {
-            sg[k] = c >= a.C0 ? 1 : 0;
+            sg[k] = (SEGU ? tw + k * a.NT : c) >= a.C0 ? 1 : 0;
             lc[k] = c - (sg[k] ? a.C0 : 0);
         }
         if (ok[k]) {
@@ -116,12 +124,26 @@ norm_quant_kernel(const NormArgs a)
         else ss0 = sumsq8<DT>(hp, ss0);
     }
 
+    // segments this wavefront holds chunks of (with SEGU a scalar fact; a
+    // segment it does not hold contributes zeros, so its reduction is skipped)
+    bool has0 = true, has1 = NSEG > 1;
+    if constexpr (NSEG > 1 && SEGU) {
+        has0 = false;
+        has1 = false;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (sg[k]) has1 = true;
+            else has0 = true;
+        }
+    }
+
     // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
     //      across the wavefronts of the row
     __shared__ float red[kMaxBlock / 64][2];
     __shared__ float redm[kMaxBlock / 64][2];
-    ss0 = sum_wave(ss0);
-    if constexpr (NSEG > 1) ss1 = sum_wave(ss1);
+    if (has0) ss0 = sum_wave(ss0);
+    if constexpr (NSEG > 1)
+        if (has1) ss1 = sum_wave(ss1);
     if (a.WPR > 1) {
         if ((tid & 63) == 0) {
             red[wave][0] = ss0;
@@ -163,8 +185,9 @@ norm_quant_kernel(const NormArgs a)
 
     // ---- quantise
     if constexpr (MODE == kPT) {
-        am0 = max_wave(am0);
-        if constexpr (NSEG > 1) am1 = max_wave(am1);
+        if (has0) am0 = max_wave(am0);
+        if constexpr (NSEG > 1)
+            if (has1) am1 = max_wave(am1);
         if (a.WPR > 1) {
             if ((tid & 63) == 0) {
                 redm[wave][0] = am0;
@@ -214,12 +237,13 @@ template <int DT, int MODE, bool GEMMA, int CPL>
 static hipError_t go_norm(const NormArgs &a, int nseg, hipStream_t st)
 {
     const int64_t blocks = (a.M + a.R - 1) / a.R;
-    if (nseg > 1)
-        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2>), dim3((unsigned)blocks),
-                           dim3(a.NT * a.R), 0, st, a);
+    const dim3 grid((unsigned)blocks), block(a.NT * a.R);
+    if (nseg == 1)
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1, false>), grid, block, 0, st, a);
+    else if (a.C0 % 64 == 0)
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1>), dim3((unsigned)blocks),
-                           dim3(a.NT * a.R), 0, st, a);
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
