@@ -21,6 +21,8 @@ Also reported, in the same JSON line:
                timed with buffer rotation so that no launch reads data
                another launch left in the 256 MB last-level cache.
   roofline     the dominant kernel against the 8 TB/s HBM peak.
+  device_copy  a 1 GiB device-to-device copy: the achievable streaming rate,
+               and the headline as a fraction of it.
   cpu_baseline the CPU oracle on a bounded sample of the headline workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu]
@@ -74,9 +76,10 @@ def two_seg_bytes(M, widths=(1536, 512)):
 
 
 # ------------------------------------------------------------------- helpers
-def _dev16(bits):
+def _dev16(bits, dtype="bf16"):
     import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
 
 
 def _src_hash():
@@ -198,17 +201,17 @@ class SiluCase:
 
 
 class TwoSegCase:
-    def __init__(self, M, *, seed, sets=1):
+    def __init__(self, M, *, seed, sets=1, dtype="bf16"):
         import torch
         import activation_fp8_quant_amd as afq
         from activation_fp8_quant_amd import inputs
         self.afq = afq
-        segs = inputs.two_segment_inputs(M, (1536, 512), seed=seed)
+        segs = inputs.two_segment_inputs(M, (1536, 512), seed=seed, dtype=dtype)
         buf = np.zeros((M, 2112), np.uint16)
         buf[:, :1536] = segs[0]["x"]
         buf[:, 1536:2048] = segs[1]["x"]
-        b = _dev16(buf)
-        self.w = [_dev16(s["w"]) for s in segs]
+        b = _dev16(buf, dtype)
+        self.w = [_dev16(s["w"], dtype) for s in segs]
         self.sets = []
         for i in range(sets):
             bi = b if i == 0 else b.clone()
@@ -227,8 +230,136 @@ class TwoSegCase:
                                          kind=self.afq.STANDARD, out=outs)
 
 
+class QuantCase:
+    """The standalone quantiser on a bf16 [M, H] activation (the separate
+    quant kernel of an unfused chain)."""
+
+    def __init__(self, M, H, *, seed, std, mode, sets=1):
+        import torch
+        import activation_fp8_quant_amd as afq
+        from activation_fp8_quant_amd import inputs
+        self.afq = afq
+        self.mode = {"mx": afq.MXFP8, "b128": afq.BLOCK128, "pt": afq.PER_TOKEN}[mode]
+        x = _dev16(inputs.to_bits(np.random.default_rng(seed).standard_normal((M, H)) * std))
+        self.sets = []
+        for i in range(sets):
+            xi = x if i == 0 else x.clone()
+            proto = afq.fp8_quant(xi, self.mode)
+            self.sets.append((xi, (proto.values, proto.scales, None)))
+        self.i = 0
+        self.bytes = M * (2 * H + H + {"mx": H // 32, "b128": 4 * (H // 128), "pt": 4}[mode])
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        x, out = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        self.afq.fp8_quant(x, self.mode, out=out)
+
+
 def rotation_sets(ws_bytes, target=1 << 30):
     return max(1, -(-target // max(ws_bytes, 1)))
+
+
+def eager_single_us(fn, reps=50):
+    """us of one launch timed alone: events around it on an idle GPU,
+    median over `reps` (includes the launch latency)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) * 1000.0)
+    return statistics.median(ts)
+
+
+# ------------------------------------------------------------- the sweep
+DECODE_M = (8, 16, 32, 64, 128, 192)
+
+
+def run_sweep():
+    """Every configuration and row count of the measurement plan, as a list
+    of records.  Hot: 200 launches over one buffer set (the pages' method;
+    the decode rows compare with their figures).  Rotated: one replay cycle
+    walks k buffer sets with k * (working set) >= 1 GiB, so that no launch
+    reads what an earlier one left in the 256 MB last-level cache; used for
+    every working set of at least 1 MiB (smaller launches are bound by
+    launch latency, and would need tens of thousands of buffer sets)."""
+    import torch
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    out = []
+
+    def rec(cfg, name, make, M, ws, *, hot=False, **extra):
+        k = 1 if hot or ws < (1 << 20) else rotation_sets(ws)
+        case = make(k)
+        us = graph_time_us(case, iters=max(200, k), reps=20 if k == 1 else 10)
+        r = {"config": cfg, "workload": name, "M": M, "us_per_launch": round(us, 2),
+             "GBps": round(case.bytes / us / 1e3, 1),
+             "cache": "hot (one buffer set)" if k == 1 else f"rotated over {k} buffer sets"}
+        if M >= 4096:
+            r["pct_hbm_peak"] = round(100 * case.bytes / us / 1e3 / HBM_PEAK_GBS, 1)
+        if "eager" in extra:
+            extra["eager_single_us"] = round(eager_single_us(case), 2)
+            del extra["eager"]
+        r.update(extra)
+        out.append(r)
+        log(f"{cfg} {name} M={M} {r['cache']}: {us:.2f} us")
+        del case
+        torch.cuda.empty_cache()
+
+    # trivial-kernel floor: a one-element fill, timed the same way
+    t = torch.zeros(1, device="cuda")
+    floor = graph_time_us(lambda: t.fill_(1.0))
+    out.append({"config": "floor", "workload": "one-element torch fill (trivial kernel)",
+                "us_per_launch": round(floor, 2), "cache": "hot (one buffer set)"})
+    log(f"trivial-kernel floor {floor:.2f} us")
+
+    c1 = "add + Gemma RMSNorm + MXFP8 + bf16 copy, H=6144"
+
+    def norm_c1(M):
+        return lambda k: NormCase(M, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal",
+                                  w_param=0.1, kind="gemma", mode="mx", normed=True, sets=k)
+
+    for M in DECODE_M:
+        ws = norm_bytes(M, 6144)
+        rec("C1", c1, norm_c1(M), M, ws, hot=True, page_us=PAGE_NORM_US[M], eager=True)
+        if ws >= (1 << 20):
+            rec("C1", c1, norm_c1(M), M, ws)
+        rec("C2", "SiLU-and-mul + MXFP8, I=768",
+            lambda k, M=M: SiluCase(M, 768, seed=0, std=2.0, mode="mx", sets=k), M,
+            silu_bytes(M, 768), hot=True, page_us_swiglu_oai=PAGE_SWIGLU_US[M], eager=True)
+        rec("f1", "standalone MXFP8 quant of a bf16 [M, 6144] (the separate quant)",
+            lambda k, M=M: QuantCase(M, 6144, seed=0, std=3.0, mode="mx", sets=k), M,
+            M * (3 * 6144 + 6144 // 32), hot=True)
+    for M in (256, 1024):
+        rec("C1", c1, norm_c1(M), M, norm_bytes(M, 6144))
+    for M in (1, 32, 256, 4096):
+        rec("C3a", "add + standard RMSNorm + 1x128, H=4096",
+            lambda k, M=M: NormCase(M, 4096, seed=0, x_std=1.0, r_std=1.0, w_kind="uniform",
+                                    w_param=0.5, kind="standard", mode="b128", normed=False, sets=k),
+            M, norm_bytes(M, 4096, normed=False, mode="b128"))
+    for M in (1, 32, 256, 4096):
+        rec("C3b", "SiLU-and-mul + 1x128, I=12288",
+            lambda k, M=M: SiluCase(M, 12288, seed=0, std=1.0, mode="b128", sets=k),
+            M, silu_bytes(M, 12288, mode="b128"))
+    for dt in ("bf16", "fp16"):
+        for M in (1, 8, 64, 1024, 8192):
+            rec("C4", f"RMSNorm + per-token, two segments 1536 + 512, {dt}",
+                lambda k, M=M, dt=dt: TwoSegCase(M, seed=0, sets=k, dtype=dt), M, two_seg_bytes(M))
+    rec("C5a", c1 + " (M = 16384 is the headline)",
+        lambda k: NormCase(4096, 6144, seed=1, x_std=3.0, r_std=3.0, w_kind="normal", w_param=0.1,
+                           kind="gemma", mode="mx", sets=k), 4096, norm_bytes(4096, 6144))
+    rec("C5b", "SiLU-and-mul + 1x128, I=3072",
+        lambda k: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128", sets=k), 16384,
+        silu_bytes(16384, 3072, mode="b128"))
+    return out
 
 
 # ----------------------------------------------------------------- CPU leg
@@ -248,9 +379,17 @@ def cpu_baseline(rows=16384):
                    mode=orc.MXFP8, eps=1e-6, threads=threads)
     dt = time.perf_counter() - t0
     b = norm_bytes(rows, H)
+    # one thread on the first 1024 rows, for the per-core rate
+    r1 = min(rows, 1024)
+    t0 = time.perf_counter()
+    orc.norm_quant(d["x"][:r1], d["w"], residual=d["r"][:r1], kind=orc.GEMMA, dtype=orc.BF16,
+                   mode=orc.MXFP8, eps=1e-6, threads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of the 16384 rows (H=6144), {dt:.2f} s wall on {threads} threads",
-            "us_per_row": round(dt * 1e6 / rows, 2)}
+            "us_per_row": round(dt * 1e6 / rows, 2),
+            "one_thread": {"GBps": round(norm_bytes(r1, H) / dt1 / 1e9, 4),
+                           "us_per_row": round(dt1 * 1e6 / r1, 1), "rows": r1}}
 
 
 # ------------------------------------------------------------------- main
@@ -296,6 +435,15 @@ def main():
     gbs = head.bytes / (ms * 1e-3) / 1e9
     print(f"[bench] headline {ms * 1e3:.2f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
+    # device-copy ceiling: torch's 1 GiB device-to-device copy (reads and
+    # writes 1 GiB), timed like the headline right after it
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = time_events(lambda: dst.copy_(src), 50, 100)
+    copy_gbs = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    print(f"[bench] 1 GiB device copy {copy_ms * 1e3:.1f} us, {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic_norm_mx_h6144_m16384.json")
     if os.path.exists(tpath):
@@ -314,6 +462,9 @@ def main():
                    "bytes_per_launch": head.bytes},
         "us_per_launch": round(ms * 1e3, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "device_copy": {"GBps": round(copy_gbs, 1), "pct_hbm_peak": round(100.0 * copy_gbs / HBM_PEAK_GBS, 1),
+                        "headline_pct_of_copy": round(100.0 * gbs / copy_gbs, 1),
+                        "method": "torch 1 GiB device-to-device copy, 100 warm-up + 50 timed, HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "norm_quant_kernel<bf16, MXFP8, Gemma, 1 chunk/lane, 1 segment>, 768 lanes per row"},
@@ -322,49 +473,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_sweep:
-        sweep = []
-        for m in (8, 16, 32, 64, 128, 192):
-            c = NormCase(m, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1,
-                         kind="gemma", mode="mx", normed=True)
-            us = graph_time_us(c)
-            s = SiluCase(m, 768, seed=0, std=2.0, mode="mx")
-            us_s = graph_time_us(s)
-            sweep.append({"workload": "norm gemma mx+copy H=6144", "M": m, "us_per_launch": round(us, 2),
-                          "GBps": round(c.bytes / us / 1e3, 1), "page_us": PAGE_NORM_US[m],
-                          "method": "graph replay 200x after >= 200 ms warm replays, median of 20"})
-            sweep.append({"workload": "silu-mul mx I=768", "M": m, "us_per_launch": round(us_s, 2),
-                          "GBps": round(s.bytes / us_s / 1e3, 1), "page_us_swiglu_oai": PAGE_SWIGLU_US[m],
-                          "method": "graph replay 200x after >= 200 ms warm replays, median of 20"})
-            print(f"[bench] M={m}: norm {us:.2f} us, silu {us_s:.2f} us", file=sys.stderr, flush=True)
-            del c, s
-        big = [
-            ("norm gemma mx+copy H=6144", lambda k: NormCase(4096, 6144, seed=1, x_std=3.0, r_std=3.0,
-                                                             w_kind="normal", w_param=0.1, kind="gemma",
-                                                             mode="mx", sets=k), norm_bytes(4096, 6144), 4096),
-            ("norm standard b128 H=4096", lambda k: NormCase(4096, 4096, seed=0, x_std=1.0, r_std=1.0,
-                                                             w_kind="uniform", w_param=0.5, kind="standard",
-                                                             mode="b128", normed=False, sets=k),
-             norm_bytes(4096, 4096, normed=False, mode="b128"), 4096),
-            ("silu-mul b128 I=12288", lambda k: SiluCase(4096, 12288, seed=0, std=1.0, mode="b128", sets=k),
-             silu_bytes(4096, 12288, mode="b128"), 4096),
-            ("two-seg per-token 1536+512", lambda k: TwoSegCase(8192, seed=0, sets=k), two_seg_bytes(8192), 8192),
-            ("silu-mul b128 I=3072", lambda k: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128", sets=k),
-             silu_bytes(16384, 3072, mode="b128"), 16384),
-        ]
-        for name, make, ws, m in big:
-            k = rotation_sets(ws)
-            c = make(k)
-            iters = max(2 * k, 20)
-            us_c = graph_time_us(c, iters=iters, reps=10)
-            sweep.append({"workload": name, "M": m, "us_per_launch": round(us_c, 2),
-                          "GBps": round(c.bytes / us_c / 1e3, 1),
-                          "pct_hbm_peak": round(100 * c.bytes / us_c / 1e3 / HBM_PEAK_GBS, 1),
-                          "method": f"graph replay of {iters} launches over {k} rotating buffer sets "
-                                    "after >= 200 ms warm replays, "
-                                    "median of 10"})
-            print(f"[bench] {name} M={m}: {us_c:.2f} us", file=sys.stderr, flush=True)
-            del c
-            torch.cuda.empty_cache()
+        sweep = run_sweep()
         result["sweep"] = sweep
 
     if not args.no_cpu:

@@ -42,7 +42,7 @@ def test_norm_modes(mode, kind, dtype, H, M):
     _report(f"{mode}-{kind}-{dtype} H={H} M={M}", check_norm(gpu, ref, mode, dtype, "norm"))
 
 
-@pytest.mark.parametrize("H", [2176, 12288, 32768, 128, 8])
+@pytest.mark.parametrize("H", [2176, 7168, 12288, 32768, 128, 8])
 def test_norm_widths(H):
     mode = "b128" if H % 128 == 0 else "pt"
     d = inputs.norm_inputs(7, H, seed=4, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
@@ -294,6 +294,37 @@ def test_fp8_quant_standalone(dtype, mode):
         assert np.array_equal(gs, s)
     else:
         assert np.array_equal(gs.view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fused_norm_equals_norm_then_quant(mode, dtype):
+    """Fused = unfused on the GPU: the fused codes and scales equal the
+    standalone quantiser applied to the fused kernel's own normed copy (the
+    quantiser's input is the dtype-rounded norm output in every mode)."""
+    M, H = 300, 6144
+    d = inputs.norm_inputs(M, H, seed=11, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1,
+                           dtype=dtype)
+    qa = afq.fused_add_rmsnorm_quant(dev16(d["x"], dtype), dev16(d["w"], dtype), 1e-6,
+                                     mode=MODE[mode], kind=afq.GEMMA, residual=dev16(d["r"], dtype),
+                                     want_normed=True)
+    sep = afq.fp8_quant(qa.normed, MODE[mode])
+    torch.cuda.synchronize()
+    assert np.array_equal(host8(qa.values), host8(sep.values))
+    assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint8),
+                          scales_u8_or_f32(sep.scales).view(np.uint8))
+
+
+def test_fused_silu_b128_equals_silu_then_quant():
+    """1x128 SiLU-and-mul quantises the bf16 activation it returns: the codes
+    equal the standalone 1x128 quantiser applied to that activation."""
+    gu = inputs.gate_up_inputs(257, 3072, seed=12, std=3.0)
+    qa = afq.silu_mul_quant(dev16(gu), afq.BLOCK128, want_act=True)
+    sep = afq.fp8_quant(qa.normed, afq.BLOCK128)
+    torch.cuda.synchronize()
+    assert np.array_equal(host8(qa.values), host8(sep.values))
+    assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint32),
+                          scales_u8_or_f32(sep.scales).view(np.uint32))
 
 
 def test_e4m3_conversion_structured_fp32():
