@@ -25,6 +25,9 @@ _SRC_PATH = os.path.join(_HERE, "afq_oracle.c")
 MXFP8, BLOCK128, PER_TOKEN = 0, 1, 2
 BF16, FP16, FP32 = 0, 1, 2
 STANDARD, GEMMA = 0, 1
+# what the quantiser reads: the path's default, the fp32 normed value (norm,
+# fp32-direct), or the bf16-rounded fp32 activation (MXFP8 SiLU, bf16-first)
+QIN_DEFAULT, QIN_FP32, QIN_BF16 = 0, 1, 2
 
 GROUP = {MXFP8: 32, BLOCK128: 128}
 
@@ -75,10 +78,10 @@ def lib():
             L.orc_quant_rows.restype = I32
             L.orc_quant_rows.argtypes = [I64, I64, P, I64, I32, I32, P, P, I64, I64, P]
             L.orc_norm_quant_rows.restype = I32
-            L.orc_norm_quant_rows.argtypes = [I64, I64, P, I64, P, P, P, I32, I32, I32,
+            L.orc_norm_quant_rows.argtypes = [I64, I64, P, I64, P, P, P, I32, I32, I32, I32,
                                               F32, P, P, P, I64, I64, P]
             L.orc_silu_quant_rows.restype = I32
-            L.orc_silu_quant_rows.argtypes = [I64, I64, P, I64, I32, P, P, P, I64, I64, P]
+            L.orc_silu_quant_rows.argtypes = [I64, I64, P, I64, I32, I32, P, P, P, I64, I64, P]
             _lib = L
     return _lib
 
@@ -183,12 +186,13 @@ def quant(x, in_dtype: int, mode: int, threads: int = 1):
 
 def norm_quant(x, weight, *, residual=None, kind: int, dtype: int, mode: int,
                eps: float, want_normed: bool = True, threads: int = 1,
-               rows=None):
+               rows=None, qin: int = QIN_DEFAULT):
     """(residual add +) RMSNorm + quantisation of x [M, H] (uint16 bit patterns).
 
     Returns dict(h=[M,H] u16 or None, values=[M,H] u8, scales, normed=u16 or None).
     `rows` optionally restricts the computation to a sorted index array of rows
-    (the other rows of every output are left zero).
+    (the other rows of every output are left zero).  qin = QIN_FP32 quantises
+    the fp32 normed value instead of the dtype-rounded row (fp32-direct).
     """
     x = np.ascontiguousarray(x, dtype=np.uint16)
     weight = np.ascontiguousarray(weight, dtype=np.uint16)
@@ -207,7 +211,7 @@ def norm_quant(x, weight, *, residual=None, kind: int, dtype: int, mode: int,
     def run_range(r0, r1):
         work = np.empty(2 * max(H, 1), np.float64)
         rc = lib().orc_norm_quant_rows(M, H, _ptr(x), H, _ptr(residual), _ptr(h),
-                                       _ptr(weight), kind, dtype, mode, float(eps),
+                                       _ptr(weight), kind, dtype, mode, qin, float(eps),
                                        _ptr(values), _ptr(scales), _ptr(normed),
                                        r0, r1, _ptr(work))
         assert rc == 0
@@ -219,15 +223,17 @@ def norm_quant(x, weight, *, residual=None, kind: int, dtype: int, mode: int,
         work = np.empty(2 * max(H, 1), np.float64)
         for r in rows:
             rc = lib().orc_norm_quant_rows(M, H, _ptr(x), H, _ptr(residual), _ptr(h),
-                                           _ptr(weight), kind, dtype, mode, float(eps),
+                                           _ptr(weight), kind, dtype, mode, qin, float(eps),
                                            _ptr(values), _ptr(scales), _ptr(normed),
                                            int(r), int(r) + 1, _ptr(work))
             assert rc == 0
     return dict(h=h, values=values, scales=scales, normed=normed)
 
 
-def silu_quant(gu, mode: int, *, want_act: bool = True, threads: int = 1, rows=None):
-    """SiLU-and-mul + quantisation of gu [M, 2I] bf16 ([gate | up])."""
+def silu_quant(gu, mode: int, *, want_act: bool = True, threads: int = 1, rows=None,
+               qin: int = QIN_DEFAULT):
+    """SiLU-and-mul + quantisation of gu [M, 2I] bf16 ([gate | up]).  With
+    MXFP8, qin = QIN_BF16 quantises the bf16-rounded activation (bf16-first)."""
     gu = np.ascontiguousarray(gu, dtype=np.uint16)
     M, two_i = gu.shape
     assert two_i % 2 == 0
@@ -238,7 +244,7 @@ def silu_quant(gu, mode: int, *, want_act: bool = True, threads: int = 1, rows=N
 
     def run_range(r0, r1):
         work = np.empty(max(I, 1), np.float64)
-        rc = lib().orc_silu_quant_rows(M, I, _ptr(gu), two_i, mode, _ptr(values),
+        rc = lib().orc_silu_quant_rows(M, I, _ptr(gu), two_i, mode, qin, _ptr(values),
                                        _ptr(scales), _ptr(act), r0, r1, _ptr(work))
         if rc != 0:
             raise ValueError("oracle: SiLU-and-mul supports the MXFP8 and 1x128 modes")

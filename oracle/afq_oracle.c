@@ -17,7 +17,8 @@
  *     fused kernels are specified as reaching that same result.
  * The only places where fp32 is used on purpose are where the pages fix it:
  * the fp32 group/token scale amax/448 and the fp32 quotient u/s that is
- * rounded to e4m3, and the fp32 SiLU-and-mul activation of the MXFP8 path.
+ * rounded to e4m3, the fp32 SiLU-and-mul activation of the MXFP8 path, and
+ * the fp32 normed value of the fp32-direct norm variant.
  *
  * Sources (the pages):
  *   [P1] vLLM pull request 65478, "MiniMax-M3.1: fuse the FFN-side MXFP8
@@ -39,6 +40,9 @@
 enum { ORC_MXFP8 = 0, ORC_BLOCK128 = 1, ORC_PER_TOKEN = 2 };
 enum { ORC_BF16 = 0, ORC_FP16 = 1, ORC_FP32 = 2 };
 enum { ORC_RMSNORM_STANDARD = 0, ORC_RMSNORM_GEMMA = 1 };
+/* What the quantiser is applied to: the default of each path, the fp32
+ * normed value (norm), or the bf16-rounded fp32 activation (MXFP8 SiLU). */
+enum { ORC_QIN_DEFAULT = 0, ORC_QIN_FP32 = 1, ORC_QIN_BF16 = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats, decoded from their field definitions.                     */
@@ -311,11 +315,22 @@ int orc_quant_rows(int64_t M, int64_t n, const void *x, int64_t x_stride, int in
  *                                        ([P2]) and per-token ([P4]) modes.
  *
  * ms, inv and y are evaluated in fp64 and rounded once to the dtype.
+ *
+ * qin = ORC_QIN_FP32, the fp32-direct variant ([P2] "Accuracy Tests": the
+ * AITER fused 1x128 norm quantises the fp32 normalized value itself, where
+ * the unfused chain first rounds it to bf16).  The pages do not give its
+ * fp32 arithmetic; it is taken in the plain order, every step rounded to
+ * fp32 once:
+ *   inv32 = fl32(1 / sqrt(ms + eps))     ms as above (fp64)
+ *   g32_j = fl32(1 + w_j) (Gemma), w_j (standard)
+ *   y_j   = fl32(fl32(h_j * inv32) * g32_j)
+ *   normed_j = RNE_dt(y_j);  (q, s) = quant(y)
+ *
  * residual / h_out may be NULL (plain RMSNorm: h = x).  normed may be NULL.
  */
 int orc_norm_quant_rows(int64_t M, int64_t H, const void *x, int64_t x_stride,
                         const void *residual, void *h_out, const void *weight,
-                        int kind, int dtype, int mode, float eps,
+                        int kind, int dtype, int mode, int qin, float eps,
                         uint8_t *values, void *scales, void *normed,
                         int64_t r0, int64_t r1, double *work /* 2H doubles */)
 {
@@ -338,12 +353,24 @@ int orc_norm_quant_rows(int64_t M, int64_t H, const void *x, int64_t x_stride,
         for (int64_t j = 0; j < H; ++j) ss += h[j] * h[j];
         double ms = ss / (double)H;
         double inv = 1.0 / sqrt(ms + (double)eps);
-        for (int64_t j = 0; j < H; ++j) {
-            double w = load_dt(weight, j, dtype);
-            double g = (kind == ORC_RMSNORM_GEMMA) ? 1.0 + w : w;
-            uint16_t uc = round_dt(h[j] * inv * g, dtype);
-            if (normed) ((uint16_t *)normed)[i * H + j] = uc;
-            u[j] = decode_dt16(uc, dtype);
+        if (qin == ORC_QIN_FP32) {
+            float inv32 = (float)inv;
+            for (int64_t j = 0; j < H; ++j) {
+                float w32 = (float)load_dt(weight, j, dtype); /* a dtype value: exact */
+                float g32 = (kind == ORC_RMSNORM_GEMMA) ? 1.0f + w32 : w32;
+                float t32 = (float)h[j] * inv32;
+                float y32 = t32 * g32;
+                if (normed) ((uint16_t *)normed)[i * H + j] = round_dt((double)y32, dtype);
+                u[j] = (double)y32;
+            }
+        } else {
+            for (int64_t j = 0; j < H; ++j) {
+                double w = load_dt(weight, j, dtype);
+                double g = (kind == ORC_RMSNORM_GEMMA) ? 1.0 + w : w;
+                uint16_t uc = round_dt(h[j] * inv * g, dtype);
+                if (normed) ((uint16_t *)normed)[i * H + j] = uc;
+                u[j] = decode_dt16(uc, dtype);
+            }
         }
         quant_row(u, H, mode, values + i * H, (uint8_t *)scales + i * spr * sb);
     }
@@ -404,9 +431,14 @@ double orc_silu(double g)
  *     a_j = RNE_bf16(RNE_bf16(silu(g_j)) * u_j), then the 1x128 quant.
  * The pages pair SiLU-and-mul with no per-token quant; that mode is rejected
  * (returns -1).  act_out (optional) receives RNE_bf16(a_j).
+ *
+ * qin = ORC_QIN_BF16 with MXFP8, the bf16-first variant: the quantiser
+ * reads RNE_bf16(a_j), the activation as the unfused chain stores it before
+ * its separate quant ([P1] "Test Plan / Correctness" and the review: the
+ * fused kernel skips that bf16 rounding, the unfused chain takes it).
  */
 int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
-                        int mode, uint8_t *values, void *scales, uint16_t *act_out,
+                        int mode, int qin, uint8_t *values, void *scales, uint16_t *act_out,
                         int64_t r0, int64_t r1, double *work /* I doubles */)
 {
     (void)M;
@@ -429,8 +461,10 @@ int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_str
                 double sg = orc_decode_bf16(round_bf16_2(shi, slo));
                 a = orc_decode_bf16(orc_round_bf16(sg * u)); /* sg*u exact in fp64 */
             }
+            uint16_t ac = orc_round_bf16(a);
+            if (mode == ORC_MXFP8 && qin == ORC_QIN_BF16) a = orc_decode_bf16(ac);
             work[j] = a;
-            if (act_out) act_out[i * I + j] = orc_round_bf16(a);
+            if (act_out) act_out[i * I + j] = ac;
         }
         quant_row(work, I, mode, values + i * I, (uint8_t *)scales + i * spr * sb);
     }

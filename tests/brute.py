@@ -173,9 +173,31 @@ def quant_fp32scale(u):
     return codes, s
 
 
-def norm_row(x_bits, r_bits, w_bits, kind, dtype, mode, eps):
+def rn_f32(v) -> Fraction:
+    """The fp32 value nearest to the exact value v (Fraction or Decimal),
+    ties to even significand; subnormals included, no overflow expected."""
+    v = Fraction(v)
+    if v == 0:
+        return v
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                      # below 2^-126 the quantum is fixed
+    q = Fraction(2) ** (e - 23)
+    n = a / q
+    k = n.numerator // n.denominator
+    rem = n - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    return k * q if v > 0 else -k * q
+
+
+def norm_row(x_bits, r_bits, w_bits, kind, dtype, mode, eps, qin="default"):
     """One row: returns dict(h, normed, codes, scales) as python ints /
-    numpy float32 scales."""
+    numpy float32 scales.  qin = "fp32": the fp32-direct variant, whose
+    quantiser reads y = fl32(fl32(h * fl32(inv)) * fl32(g)) (each step one
+    exact rounding to fp32) and whose copy is that y rounded to the dtype."""
     H = len(x_bits)
     x = [frac_of_bits16(b, dtype) for b in x_bits]
     w = [frac_of_bits16(b, dtype) for b in w_bits]
@@ -190,12 +212,21 @@ def norm_row(x_bits, r_bits, w_bits, kind, dtype, mode, eps):
     den = Decimal(ms.numerator) / Decimal(ms.denominator) + Decimal(float(np.float32(eps)))
     inv = 1 / den.sqrt()
     u_codes, u = [], []
-    for hv, wv in zip(h, w):
-        g = (1 + wv) if kind == "gemma" else wv
-        y = Decimal(hv.numerator) / Decimal(hv.denominator) * inv * (Decimal(g.numerator) / Decimal(g.denominator))
-        c, val = round16(y, dtype)
-        u_codes.append(c)
-        u.append(val)
+    if qin == "fp32":
+        inv32 = rn_f32(inv)
+        for hv, wv in zip(h, w):
+            g32 = rn_f32(1 + wv) if kind == "gemma" else wv
+            y = rn_f32(rn_f32(hv * inv32) * g32)
+            c, _ = round16(y, dtype)
+            u_codes.append(c)
+            u.append(y)
+    else:
+        for hv, wv in zip(h, w):
+            g = (1 + wv) if kind == "gemma" else wv
+            y = Decimal(hv.numerator) / Decimal(hv.denominator) * inv * (Decimal(g.numerator) / Decimal(g.denominator))
+            c, val = round16(y, dtype)
+            u_codes.append(c)
+            u.append(val)
     codes, scales = [], []
     G = 32 if mode == "mx" else 128 if mode == "b128" else H
     for k in range(0, H, G):

@@ -35,6 +35,43 @@ def test_norm_quant_matches_exact_brute_force(mode, kind, dtype, H):
                                   np.array(ref["scales"], np.float32).view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", ["b128", "pt"])
+@pytest.mark.parametrize("kind", ["gemma", "standard"])
+@pytest.mark.parametrize("dtype,H", [("bf16", 128), ("fp16", 128), ("bf16", 384)])
+def test_fp32_direct_norm_matches_exact_brute_force(mode, kind, dtype, H):
+    """The fp32-direct variant: y = fl32(fl32(h * fl32(inv)) * fl32(g)) with
+    every rounding taken exactly in rational arithmetic (inv from a 60-digit
+    square root), quantised as fp32; the copy is y rounded to the dtype."""
+    M = 3
+    d = inputs.norm_inputs(M, H, seed=13, x_std=3.0, r_std=1.0,
+                           w_kind="normal" if kind == "gemma" else "uniform",
+                           w_param=0.1 if kind == "gemma" else 0.5, dtype=dtype)
+    out = orc.norm_quant(d["x"], d["w"], residual=d["r"], kind=KINDS[kind], dtype=DTYPES[dtype],
+                         mode=MODES[mode], eps=1e-6, qin=orc.QIN_FP32)
+    for i in range(M):
+        ref = brute.norm_row(d["x"][i], d["r"][i], d["w"], kind, dtype, mode, 1e-6, qin="fp32")
+        assert list(out["h"][i]) == ref["h"]
+        assert list(out["normed"][i]) == ref["normed"]
+        assert np.array_equal(ord8(out["values"][i]), ord8(np.array(ref["codes"], np.uint8)))
+        assert np.array_equal(out["scales"][i].view(np.uint32),
+                              np.array(ref["scales"], np.float32).view(np.uint32))
+
+
+def test_fp32_direct_differs_from_default_by_at_most_one_step():
+    """Quantising the fp32 normed value instead of its dtype rounding moves
+    the group amax by less than a bf16 half-ulp and each quotient by less
+    than one e4m3 step: codes differ by at most one step, and only a few %
+    of them ([P2] "Accuracy Tests" reports about 2.2 %)."""
+    d = inputs.norm_inputs(64, 4096, seed=14, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    kw = dict(residual=d["r"], kind=orc.STANDARD, dtype=orc.BF16, mode=orc.BLOCK128, eps=1e-6)
+    a = orc.norm_quant(d["x"], d["w"], **kw)
+    b = orc.norm_quant(d["x"], d["w"], qin=orc.QIN_FP32, **kw)
+    diff = np.abs(ord8(a["values"]).astype(np.int64) - ord8(b["values"]).astype(np.int64))
+    assert diff.max() <= 1
+    assert 0.005 < (diff == 1).mean() < 0.05
+    assert np.array_equal(a["h"], b["h"])
+
+
 def test_norm_without_residual_matches_brute_force():
     d = inputs.norm_inputs(2, 128, seed=12, x_std=1.0, r_std=None, w_kind="uniform", w_param=0.5)
     out = orc.norm_quant(d["x"], d["w"], residual=None, kind=orc.STANDARD, dtype=orc.BF16,

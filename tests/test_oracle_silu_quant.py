@@ -118,6 +118,32 @@ def test_silu_quant_matches_brute_force(mode):
             assert np.array_equal(out["scales"][i], np.array(scales, np.float32))
 
 
+def test_silu_mx_bf16_first_matches_brute_force():
+    """The bf16-first MXFP8 variant quantises RNE_bf16(fl32(silu(g) u)), the
+    activation as the unfused chain stores it (decimal silu, exact roundings,
+    brute-force MX quantiser)."""
+    I = 256
+    gu = inputs.gate_up_inputs(2, I, seed=23, std=2.0)
+    out = orc.silu_quant(gu, orc.MXFP8, qin=orc.QIN_BF16)
+    for i in range(2):
+        a = []
+        for gb, ub in zip(gu[i, :I], gu[i, I:]):
+            gf = brute.frac_of_bits16(gb, "bf16")
+            uf = brute.frac_of_bits16(ub, "bf16")
+            v = _silu_exact(gf) * (Decimal(uf.numerator) / Decimal(uf.denominator))
+            _, ab = brute.round16(brute.rn_f32(v), "bf16")
+            a.append(ab)
+        codes, scales = [], []
+        for k in range(0, I, 32):
+            q, s = brute.quant_mx(a[k:k + 32])
+            codes += q
+            scales.append(s)
+        assert np.array_equal(ord8(out["values"][i]), ord8(np.array(codes, np.uint8)))
+        assert list(out["scales"][i]) == scales
+    # the optional bf16 copy is the same in both variants
+    assert np.array_equal(out["act"], orc.silu_quant(gu, orc.MXFP8)["act"])
+
+
 def test_silu_per_token_rejected():
     gu = inputs.gate_up_inputs(1, 128, seed=1, std=1.0)
     with pytest.raises(ValueError):
