@@ -21,6 +21,7 @@ import torch  # loaded first: the library then binds to torch's HIP runtime
 
 __all__ = [
     "MXFP8", "BLOCK128", "PER_TOKEN", "STANDARD", "GEMMA",
+    "QIN_DEFAULT", "QIN_FP32", "QIN_BF16",
     "QuantizedActivation", "AfqError",
     "fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant",
     "abi_version", "status_string", "library_path", "load",
@@ -29,6 +30,9 @@ __all__ = [
 # ---------------------------------------------------------------- constants
 MXFP8, BLOCK128, PER_TOKEN = 0, 1, 2
 STANDARD, GEMMA = 0, 1
+# what the quantiser reads: the path's default, the fp32 normed value (norm,
+# 1x128 / per-token), or the bf16-rounded activation (SiLU-and-mul, MXFP8)
+QIN_DEFAULT, QIN_FP32, QIN_BF16 = 0, 1, 2
 _BF16, _FP16, _FP32 = 0, 1, 2
 _DTYPE_TAG = {torch.bfloat16: _BF16, torch.float16: _FP16, torch.float32: _FP32}
 _MODE_NAMES = {"mxfp8": MXFP8, "mx": MXFP8, "block128": BLOCK128, "b128": BLOCK128,
@@ -61,14 +65,14 @@ class _NormSeg(ctypes.Structure):
 class _NormDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("nseg", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("reserved", ctypes.c_int32), ("residual_in", ctypes.c_void_p),
+                ("quant_input", ctypes.c_int32), ("residual_in", ctypes.c_void_p),
                 ("residual_out", ctypes.c_void_p), ("seg", _NormSeg * 2)]
 
 
 class _ActDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("I", ctypes.c_int64), ("gate_up", ctypes.c_void_p),
                 ("gate_up_row_stride", ctypes.c_int64), ("mode", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("out", _QAct)]
+                ("quant_input", ctypes.c_int32), ("out", _QAct)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -220,6 +224,7 @@ def fused_add_rmsnorm_quant(
     residual_out: Optional[torch.Tensor] = None,
     inplace: bool = False,
     want_normed: bool = False,
+    quant_input: int = QIN_DEFAULT,
     out=None,
     stream=None,
 ):
@@ -232,6 +237,8 @@ def fused_add_rmsnorm_quant(
                  goes to residual_out (a new tensor by default, `residual`
                  itself with inplace=True).
     want_normed  also return the normed rows rounded to the input dtype.
+    quant_input  QIN_DEFAULT: quantise the dtype-rounded normed rows;
+                 QIN_FP32 (1x128 / per-token): quantise the fp32 normed value.
     out          optional preallocated (values, scales, normed) per segment
                  (a tuple, or a list of tuples for two segments).
     Returns a QuantizedActivation, or a list of two for two segments.
@@ -252,6 +259,7 @@ def fused_add_rmsnorm_quant(
     d = _NormDesc()
     d.M, d.nseg, d.kind, d.dtype, d.mode = M, len(xs), kind, _DTYPE_TAG[dtype], mode
     d.eps = float(eps)
+    d.quant_input = int(quant_input)
     results = []
     for i, (xi, wi) in enumerate(zip(xs, ws)):
         _rowmajor(xi, "x")
@@ -283,12 +291,13 @@ def fused_add_rmsnorm_quant(
 
 
 def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
-                   out=None, stream=None) -> QuantizedActivation:
+                   quant_input: int = QIN_DEFAULT, out=None, stream=None) -> QuantizedActivation:
     """SiLU-and-mul of a bf16 [M, 2I] row ([gate | up]) + FP8 quantisation.
 
     MXFP8 quantises the fp32 activation; BLOCK128 rounds silu and the product
-    to bf16 first (the unfused SiluAndMul).  want_act also returns the bf16
-    activation.
+    to bf16 first (the unfused SiluAndMul).  With MXFP8, quant_input=QIN_BF16
+    quantises the bf16-rounded activation instead (the unfused chain's
+    rounding).  want_act also returns the bf16 activation.
     """
     lib = load()
     mode = _mode(mode)
@@ -303,6 +312,7 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
                                      torch.bfloat16 if want_act else None, out)
     d = _ActDesc()
     d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
+    d.quant_input = int(quant_input)
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
     st = lib.silu_mul_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, gate_up.device)))
     if st != 0:

@@ -36,6 +36,7 @@ bool overlap(const Span &a, const Span &b)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+bool valid_qin(int q) { return q == AFQ_QIN_DEFAULT || q == AFQ_QIN_FP32 || q == AFQ_QIN_BF16; }
 int group_of(int mode) { return mode == AFQ_MXFP8 ? 32 : mode == AFQ_BLOCK128 ? 128 : 8; }
 
 int64_t scale_cols(int mode, int64_t cols)
@@ -90,8 +91,8 @@ const char *afq_status_string(int status)
     case AFQ_ERR_ALIGN: return "pointer or row pitch not aligned (16 bytes; scales 4 bytes)";
     case AFQ_ERR_DTYPE: return "dtype not supported by this entry point";
     case AFQ_ERR_ALIAS: return "an output overlaps another output or an input";
-    case AFQ_ERR_UNSUPPORTED: return "quantisation mode or norm kind not supported by this entry point";
-    case AFQ_ERR_ARG: return "invalid argument (eps, enum value or reserved field)";
+    case AFQ_ERR_UNSUPPORTED: return "quantisation mode, norm kind or quant_input not supported by this entry point";
+    case AFQ_ERR_ARG: return "invalid argument (eps or an enum value)";
     case AFQ_ERR_LAUNCH: return "HIP kernel launch failed (see afq_last_hip_error)";
     default: return "unknown status";
     }
@@ -100,13 +101,15 @@ const char *afq_status_string(int status)
 int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
 {
     if (!d) return AFQ_ERR_NULL;
-    if (d->reserved != 0) return AFQ_ERR_ARG;
+    if (!valid_qin(d->quant_input)) return AFQ_ERR_ARG;
     if (!valid_mode(d->mode)) return AFQ_ERR_ARG;
     if (d->kind != AFQ_RMSNORM_STANDARD && d->kind != AFQ_RMSNORM_GEMMA) return AFQ_ERR_ARG;
     if (d->dtype != AFQ_BF16 && d->dtype != AFQ_FP16) {
         return (d->dtype == AFQ_FP32) ? AFQ_ERR_DTYPE : AFQ_ERR_ARG;
     }
     if (!(std::isfinite(d->eps) && d->eps >= 0.0f)) return AFQ_ERR_ARG;
+    if (d->quant_input == AFQ_QIN_BF16) return AFQ_ERR_UNSUPPORTED;
+    if (d->quant_input == AFQ_QIN_FP32 && d->mode == AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
     if (d->M < 0) return AFQ_ERR_SHAPE;
     if (d->nseg != 1 && d->nseg != 2) return AFQ_ERR_SHAPE;
     const bool has_res = d->residual_in != nullptr || d->residual_out != nullptr;
@@ -184,15 +187,18 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
     p.kind = d->kind;
     p.dtype = d->dtype;
     p.mode = d->mode;
+    p.qin = d->quant_input;
     return launched(afq::launch_norm(p, stream));
 }
 
 int silu_mul_quant(const afq_act_desc *d, void *stream)
 {
     if (!d) return AFQ_ERR_NULL;
-    if (d->reserved != 0) return AFQ_ERR_ARG;
+    if (!valid_qin(d->quant_input)) return AFQ_ERR_ARG;
     if (!valid_mode(d->mode)) return AFQ_ERR_ARG;
     if (d->mode == AFQ_PER_TOKEN) return AFQ_ERR_UNSUPPORTED;
+    if (d->quant_input == AFQ_QIN_FP32) return AFQ_ERR_UNSUPPORTED;
+    if (d->quant_input == AFQ_QIN_BF16 && d->mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
     if (d->M < 0) return AFQ_ERR_SHAPE;
     if (!width_ok(d->I, d->mode)) return AFQ_ERR_SHAPE;
     if (d->gate_up_row_stride < 2 * d->I) return AFQ_ERR_SHAPE;
@@ -221,6 +227,7 @@ int silu_mul_quant(const afq_act_desc *d, void *stream)
     p.M = M;
     p.I = (int32_t)I;
     p.mode = d->mode;
+    p.qin = d->quant_input;
     return launched(afq::launch_act(p, stream));
 }
 

@@ -140,7 +140,10 @@ __device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8],
     stg_stream(a.values + out_off, q);
 }
 
-template <int MODE, int CPL>
+// QBF16 (MXFP8 only): the bf16-first variant, which quantises the fp32
+// activation rounded to bf16 (the value the unfused chain stores and then
+// quantises) instead of the fp32 activation itself.
+template <int MODE, int CPL, bool QBF16>
 __global__ void __launch_bounds__(256)
 act_quant_kernel(const ActArgs a)
 {
@@ -175,7 +178,8 @@ act_quant_kernel(const ActArgs a)
             silu_f32x8(g, sg);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] *= sg[i];
-            if (a.act) stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
+            const uint4 ap = QBF16 ? round8<kBF16>(v) : pack8<kBF16>(v);
+            if (a.act) stg_stream(a.act + out_off * 2, ap);
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
             if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
@@ -189,11 +193,11 @@ act_quant_kernel(const ActArgs a)
 }
 
 // ================================================================ launcher
-template <int MODE, int CPL>
+template <int MODE, int CPL, bool QBF16>
 static hipError_t go_act(const ActArgs &a, hipStream_t st)
 {
     const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
-    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL, QBF16>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -214,7 +218,9 @@ int launch_act(const ActPlan &p, void *stream)
         a.I = p.I;
         a.total = (uint32_t)(rows * C);
         a.dc = divc((uint32_t)C);
-        hipError_t e = p.mode == kMX ? go_act<kMX, 1>(a, st) : go_act<kB128, 1>(a, st);
+        hipError_t e = p.mode != kMX ? go_act<kB128, 1, false>(a, st)
+                     : p.qin == 2   ? go_act<kMX, 1, true>(a, st)
+                                    : go_act<kMX, 1, false>(a, st);
         if (e != hipSuccess) return (int)e;
     }
     return 0;

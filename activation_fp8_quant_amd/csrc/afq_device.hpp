@@ -185,6 +185,36 @@ __device__ __forceinline__ float max_xor32(float v)
 
 // all-reduce over the 64 lanes of a wavefront (no LDS traffic)
 __device__ __forceinline__ float sum_wave(float v) { return sum_xor32(sum_xor16(sum_row16(v))); }
+
+// fp64 all-reduce over a wavefront: the same lane pairings as sum_wave,
+// with each exchange applied to both 32-bit halves of the double (a lane
+// permutation moves the two halves together).  Every lane ends with the
+// same value: each step adds two partials that are equal across the pair.
+__device__ __forceinline__ double join64(uint32_t lo, uint32_t hi)
+{
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    return join64(dppu<CTRL>((uint32_t)b), dppu<CTRL>((uint32_t)(b >> 32)));
+}
+__device__ __forceinline__ double sum_wave_f64(double v)
+{
+    v += dppd<kQuadSwap1>(v);
+    v += dppd<kQuadSwap2>(v);
+    v += dppd<kRowHalfMirror>(v);
+    v += dppd<kRowMirror>(v);
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = join64(lo[0], hi[0]) + join64(lo[1], hi[1]);
+    b = __builtin_bit_cast(uint64_t, v);
+    lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    return join64(lo[0], hi[0]) + join64(lo[1], hi[1]);
+}
 __device__ __forceinline__ float max_wave(float v) { return max_xor32(max_xor16(max_row16(v))); }
 
 // Block barrier that orders only LDS: the waves exchange reduction

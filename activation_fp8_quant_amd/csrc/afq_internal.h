@@ -27,6 +27,7 @@ struct NormPlan {
     int32_t kind;           // 0 standard, 1 Gemma
     int32_t dtype;          // 0 bf16, 1 fp16
     int32_t mode;           // 0 MX, 1 B128, 2 PT
+    int32_t qin;            // 0 dtype-rounded row, 1 fp32 normed value (B128 / PT)
 };
 
 struct ActPlan {
@@ -38,6 +39,7 @@ struct ActPlan {
     int64_t M;
     int32_t I;
     int32_t mode;
+    int32_t qin;            // 0 mode default, 2 bf16-rounded activation (MX)
 };
 
 struct QuantPlan {

@@ -55,12 +55,20 @@ __device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
     return acc;
 }
 
+// F32Q (1x128 / per-token): the fp32-direct variant.  The quantiser reads
+// the fp32 normed value y = fl32(fl32(h * inv32) * g32) instead of its
+// dtype rounding, with inv32 = fl32(1 / sqrt(mean(h^2) + eps)).  To make
+// inv32 the correctly rounded value (so that y, and with it every scale and
+// code, is reproducible) the sum of squares is accumulated in fp64 (each
+// h^2 is exact there) and the square root and reciprocal are fp64 IEEE
+// operations rounded once to fp32.
+//
 // SEGU (two segments only): the first segment's chunk count C0 is a
 // multiple of 64, so the chunks of slot k of a wavefront (64 consecutive
 // chunks starting at a multiple of 64) all lie in one segment; the segment
 // of each slot is then known per wavefront (scalar registers), and a
 // wavefront skips the reductions of a segment it holds no chunk of.
-template <int DT, int MODE, bool GEMMA, int CPL, int NSEG, bool SEGU>
+template <int DT, int MODE, bool GEMMA, int CPL, int NSEG, bool SEGU, bool F32Q>
 __global__ void __launch_bounds__(kMaxBlock)
 norm_quant_kernel(const NormArgs a)
 {
@@ -106,6 +114,7 @@ norm_quant_kernel(const NormArgs a)
     // ---- residual add (h = round_dt(x + r), stored), sum of squares
     float h[CPL][8];
     float ss0 = 0.f, ss1 = 0.f;
+    double sd0 = 0.0, sd1 = 0.0; // F32Q
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
@@ -120,8 +129,16 @@ norm_quant_kernel(const NormArgs a)
             stg_stream(a.res_out + rrow + lc[k] * 16, hp);
         }
         unpack8<DT>(hp, h[k]);
-        if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
-        else ss0 = sumsq8<DT>(hp, ss0);
+        if constexpr (F32Q) {
+            double sd = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sd = __builtin_fma((double)h[k][i], (double)h[k][i], sd);
+            if (NSEG > 1 && sg[k]) sd1 += sd;
+            else sd0 += sd;
+        } else {
+            if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
+            else ss0 = sumsq8<DT>(hp, ss0);
+        }
     }
 
     // segments this wavefront holds chunks of (with SEGU a scalar fact; a
@@ -139,29 +156,54 @@ norm_quant_kernel(const NormArgs a)
 
     // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
     //      across the wavefronts of the row
-    __shared__ float red[kMaxBlock / 64][2];
     __shared__ float redm[kMaxBlock / 64][2];
-    if (has0) ss0 = sum_wave(ss0);
-    if constexpr (NSEG > 1)
-        if (has1) ss1 = sum_wave(ss1);
-    if (a.WPR > 1) {
-        if ((tid & 63) == 0) {
-            red[wave][0] = ss0;
-            if constexpr (NSEG > 1) red[wave][1] = ss1;
+    float inv0, inv1;
+    if constexpr (F32Q) {
+        __shared__ double redd[kMaxBlock / 64][2];
+        if (has0) sd0 = sum_wave_f64(sd0);
+        if constexpr (NSEG > 1)
+            if (has1) sd1 = sum_wave_f64(sd1);
+        if (a.WPR > 1) {
+            if ((tid & 63) == 0) {
+                redd[wave][0] = sd0;
+                if constexpr (NSEG > 1) redd[wave][1] = sd1;
+            }
+            lds_barrier();
+            sd0 = 0.0;
+            sd1 = 0.0;
+            for (int i = 0; i < a.WPR; ++i) {
+                sd0 += redd[rib * a.WPR + i][0];
+                if constexpr (NSEG > 1) sd1 += redd[rib * a.WPR + i][1];
+            }
         }
-        lds_barrier();
-        ss0 = 0.f;
-        ss1 = 0.f;
-        for (int i = 0; i < a.WPR; ++i) {
-            ss0 += red[rib * a.WPR + i][0];
-            if constexpr (NSEG > 1) ss1 += red[rib * a.WPR + i][1];
+        inv0 = (float)(1.0 / sqrt(sd0 / (double)a.seg[0].cols + (double)a.eps));
+        inv1 = NSEG > 1 ? (float)(1.0 / sqrt(sd1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
+    } else {
+        __shared__ float red[kMaxBlock / 64][2];
+        if (has0) ss0 = sum_wave(ss0);
+        if constexpr (NSEG > 1)
+            if (has1) ss1 = sum_wave(ss1);
+        if (a.WPR > 1) {
+            if ((tid & 63) == 0) {
+                red[wave][0] = ss0;
+                if constexpr (NSEG > 1) red[wave][1] = ss1;
+            }
+            lds_barrier();
+            ss0 = 0.f;
+            ss1 = 0.f;
+            for (int i = 0; i < a.WPR; ++i) {
+                ss0 += red[rib * a.WPR + i][0];
+                if constexpr (NSEG > 1) ss1 += red[rib * a.WPR + i][1];
+            }
         }
+        inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
+        inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
     }
-    const float inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
-    const float inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
 
     // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
-    //      Gemma: g * inv = (1 + w) inv as one FMA.
+    //      Gemma: g * inv = (1 + w) inv as one FMA.  F32Q: y = (h inv) g
+    //      in that order is kept in place of h (the quantiser's input), and
+    //      only the copy is rounded.
     float am0 = 0.f, am1 = 0.f;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
@@ -169,10 +211,18 @@ norm_quant_kernel(const NormArgs a)
         const float inv = sg[k] ? inv1 : inv0;
         float wf[8];
         unpack8<DT>(wv[k], wf);
+        if constexpr (F32Q) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
-        const uint4 up = round8<DT>(h[k]);
+            for (int i = 0; i < 8; ++i) {
+                const float g = GEMMA ? 1.0f + wf[i] : wf[i];
+                h[k][i] = (h[k][i] * inv) * g;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
+        }
+        const uint4 up = F32Q ? pack8<DT>(h[k]) : round8<DT>(h[k]);
         uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
         const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
         if (normed)
@@ -233,45 +283,52 @@ norm_quant_kernel(const NormArgs a)
 }
 
 // ================================================================ launcher
-template <int DT, int MODE, bool GEMMA, int CPL>
+template <int DT, int MODE, bool GEMMA, int CPL, bool F32Q>
 static hipError_t go_norm(const NormArgs &a, int nseg, hipStream_t st)
 {
     const int64_t blocks = (a.M + a.R - 1) / a.R;
     const dim3 grid((unsigned)blocks), block(a.NT * a.R);
     if (nseg == 1)
-        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 1, false, F32Q>), grid, block, 0, st, a);
     else if (a.C0 % 64 == 0)
-        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, true, F32Q>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((norm_quant_kernel<DT, MODE, GEMMA, CPL, 2, false, F32Q>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, int MODE, bool GEMMA>
+template <int DT, int MODE, bool GEMMA, bool F32Q>
 static hipError_t go_norm_cpl(const NormArgs &a, int nseg, int CPL, hipStream_t st)
 {
     switch (CPL) {
-    case 1: return go_norm<DT, MODE, GEMMA, 1>(a, nseg, st);
-    case 2: return go_norm<DT, MODE, GEMMA, 2>(a, nseg, st);
-    case 3: return go_norm<DT, MODE, GEMMA, 3>(a, nseg, st);
-    default: return go_norm<DT, MODE, GEMMA, 4>(a, nseg, st);
+    case 1: return go_norm<DT, MODE, GEMMA, 1, F32Q>(a, nseg, st);
+    case 2: return go_norm<DT, MODE, GEMMA, 2, F32Q>(a, nseg, st);
+    case 3: return go_norm<DT, MODE, GEMMA, 3, F32Q>(a, nseg, st);
+    default: return go_norm<DT, MODE, GEMMA, 4, F32Q>(a, nseg, st);
     }
 }
 
-template <int DT, int MODE>
+template <int DT, int MODE, bool F32Q>
 static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int nseg, int CPL, hipStream_t st)
 {
-    return gemma ? go_norm_cpl<DT, MODE, true>(a, nseg, CPL, st)
-                 : go_norm_cpl<DT, MODE, false>(a, nseg, CPL, st);
+    return gemma ? go_norm_cpl<DT, MODE, true, F32Q>(a, nseg, CPL, st)
+                 : go_norm_cpl<DT, MODE, false, F32Q>(a, nseg, CPL, st);
 }
 
+// The fp32-direct variant exists for the 1x128 and per-token modes only
+// (the C ABI rejects it with MXFP8).
 template <int DT>
-static hipError_t go_norm_mode(const NormArgs &a, int mode, bool gemma, int nseg, int CPL, hipStream_t st)
+static hipError_t go_norm_mode(const NormArgs &a, int mode, bool f32q, bool gemma, int nseg, int CPL,
+                               hipStream_t st)
 {
     switch (mode) {
-    case kMX: return go_norm_kind<DT, kMX>(a, gemma, nseg, CPL, st);
-    case kB128: return go_norm_kind<DT, kB128>(a, gemma, nseg, CPL, st);
-    default: return go_norm_kind<DT, kPT>(a, gemma, nseg, CPL, st);
+    case kMX: return go_norm_kind<DT, kMX, false>(a, gemma, nseg, CPL, st);
+    case kB128:
+        return f32q ? go_norm_kind<DT, kB128, true>(a, gemma, nseg, CPL, st)
+                    : go_norm_kind<DT, kB128, false>(a, gemma, nseg, CPL, st);
+    default:
+        return f32q ? go_norm_kind<DT, kPT, true>(a, gemma, nseg, CPL, st)
+                    : go_norm_kind<DT, kPT, false>(a, gemma, nseg, CPL, st);
     }
 }
 
@@ -295,8 +352,9 @@ int launch_norm(const NormPlan &p, void *stream)
     a.inv_cols1 = 1.0f / (float)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
-    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, gemma, p.nseg, sh.CPL, st)
-                                    : go_norm_mode<kBF16>(a, p.mode, gemma, p.nseg, sh.CPL, st);
+    const bool f32q = p.qin == 1;
+    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, f32q, gemma, p.nseg, sh.CPL, st)
+                                    : go_norm_mode<kBF16>(a, p.mode, f32q, gemma, p.nseg, sh.CPL, st);
     return (int)e;
 }
 

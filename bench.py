@@ -146,7 +146,7 @@ class NormCase:
     """Preallocated buffers of one fused-norm workload (k rotation sets)."""
 
     def __init__(self, M, H, *, seed, x_std, r_std, w_kind, w_param, kind, mode,
-                 normed=True, sets=1):
+                 normed=True, sets=1, qin=0):
         import torch
         import activation_fp8_quant_amd as afq
         from activation_fp8_quant_amd import inputs
@@ -162,10 +162,11 @@ class NormCase:
             xi = x if i == 0 else x.clone()
             ri = None if r is None else (r if i == 0 else r.clone())
             proto = afq.fused_add_rmsnorm_quant(xi, w, 1e-6, mode=self.mode, kind=self.kind,
-                                                residual=ri, want_normed=normed)
+                                                residual=ri, want_normed=normed, quant_input=qin)
             self.sets.append(dict(x=xi, r=ri, out=(proto.values, proto.scales, proto.normed),
                                   rout=proto.residual))
         self.w = w
+        self.qin = qin
         self.i = 0
         self.bytes = norm_bytes(M, H, residual=r is not None, normed=normed, mode=mode)
         torch.cuda.synchronize()
@@ -174,11 +175,12 @@ class NormCase:
         s = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
         self.afq.fused_add_rmsnorm_quant(s["x"], self.w, 1e-6, mode=self.mode, kind=self.kind,
-                                         residual=s["r"], residual_out=s["rout"], out=s["out"])
+                                         residual=s["r"], residual_out=s["rout"], out=s["out"],
+                                         quant_input=self.qin)
 
 
 class SiluCase:
-    def __init__(self, M, I, *, seed, std, mode, sets=1):
+    def __init__(self, M, I, *, seed, std, mode, sets=1, qin=0):
         import torch
         import activation_fp8_quant_amd as afq
         from activation_fp8_quant_amd import inputs
@@ -188,8 +190,9 @@ class SiluCase:
         self.sets = []
         for i in range(sets):
             gi = gu if i == 0 else gu.clone()
-            proto = afq.silu_mul_quant(gi, self.mode)
+            proto = afq.silu_mul_quant(gi, self.mode, quant_input=qin)
             self.sets.append((gi, (proto.values, proto.scales, None)))
+        self.qin = qin
         self.i = 0
         self.bytes = silu_bytes(M, I, mode=mode)
         torch.cuda.synchronize()
@@ -197,7 +200,7 @@ class SiluCase:
     def __call__(self):
         g, out = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
-        self.afq.silu_mul_quant(g, self.mode, out=out)
+        self.afq.silu_mul_quant(g, self.mode, out=out, quant_input=self.qin)
 
 
 class TwoSegCase:
@@ -356,6 +359,18 @@ def run_sweep():
     rec("C5a", c1 + " (M = 16384 is the headline)",
         lambda k: NormCase(4096, 6144, seed=1, x_std=3.0, r_std=3.0, w_kind="normal", w_param=0.1,
                            kind="gemma", mode="mx", sets=k), 4096, norm_bytes(4096, 6144))
+    # rounding-point variants: fp32-direct 1x128 norm, bf16-first MXFP8 SiLU
+    import activation_fp8_quant_amd as afq
+    for M in (32, 4096):
+        rec("f2", "add + standard RMSNorm + 1x128, fp32-direct (quantise the fp32 normed value), H=4096",
+            lambda k, M=M: NormCase(M, 4096, seed=0, x_std=1.0, r_std=1.0, w_kind="uniform",
+                                    w_param=0.5, kind="standard", mode="b128", normed=False, sets=k,
+                                    qin=afq.QIN_FP32),
+            M, norm_bytes(M, 4096, normed=False, mode="b128"))
+    for M in (8, 192):
+        rec("f2", "SiLU-and-mul + MXFP8, bf16-first (quantise the bf16 activation), I=768",
+            lambda k, M=M: SiluCase(M, 768, seed=0, std=2.0, mode="mx", sets=k, qin=afq.QIN_BF16), M,
+            silu_bytes(M, 768), hot=True)
     rec("C5b", "SiLU-and-mul + 1x128, I=3072",
         lambda k: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128", sets=k), 16384,
         silu_bytes(16384, 3072, mode="b128"))

@@ -41,6 +41,13 @@
  *             (an all-zero group stores s = 0 and codes 0x00)
  *   e4m3 rounding is round-to-nearest-even on OCP e4m3fn (max 448,
  *   subnormals k * 2^-9, sign in bit 7).
+ * fp32-direct variant (quant_input = AFQ_QIN_FP32; 1x128 and per-token):
+ *   the quantiser reads the fp32 normed value instead of its dtype rounding
+ *   (the reading of AITER's fused 1x128 norm in SGLang pull request 48043,
+ *   "Accuracy Tests"), in this order, every step rounded to fp32 once:
+ *     inv32 = fl32(1 / sqrt(mean(h^2) + eps))  (mean(h^2) accumulated in fp64)
+ *     y     = fl32(fl32(h * inv32) * g32)      g32 = fl32(1 + w) or w
+ *     normed copy = round_dt(y);  s, q from y as above.
  * The norm itself is evaluated in fp32; the quantiser acts on the rounded
  * row u, so the result equals the unfused norm -> quant composition (vLLM
  * pull request 65478, "Test Plan / Correctness").
@@ -52,6 +59,10 @@
  *   BLOCK128: a_j = bf16(bf16(silu(gate_j)) * up_j), the rounding of the
  *             unfused SiluAndMul, so the codes equal the unfused chain
  *             (SGLang pull request 48043, "Modifications")
+ *   MXFP8 with quant_input = AFQ_QIN_BF16 (bf16-first variant): a_j is
+ *             rounded to bf16 before the quantiser, as the unfused
+ *             SiLU-and-mul -> quant chain stores it (vLLM pull request
+ *             65478, "Test Plan / Correctness").
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless stated otherwise; descriptors are
@@ -80,7 +91,7 @@
 extern "C" {
 #endif
 
-#define AFQ_ABI_VERSION 1
+#define AFQ_ABI_VERSION 2
 
 /* Return codes. */
 enum {
@@ -95,8 +106,10 @@ enum {
     AFQ_ERR_DTYPE = -4,       /* dtype not allowed for this entry point */
     AFQ_ERR_ALIAS = -5,       /* an output overlaps another output or an input
                                  (residual_out == residual_in is allowed) */
-    AFQ_ERR_UNSUPPORTED = -6, /* mode / kind not offered by this entry point */
-    AFQ_ERR_ARG = -7,         /* eps negative or not finite, unknown enum value */
+    AFQ_ERR_UNSUPPORTED = -6, /* mode, kind or quant_input not offered by this
+                                 entry point (for this mode) */
+    AFQ_ERR_ARG = -7,         /* eps negative or not finite, unknown enum value
+                                 (quant_input included) */
     AFQ_ERR_LAUNCH = -8       /* the HIP launch failed; see afq_last_hip_error() */
 };
 
@@ -106,6 +119,16 @@ enum { AFQ_MXFP8 = 0, AFQ_BLOCK128 = 1, AFQ_PER_TOKEN = 2 };
 enum { AFQ_BF16 = 0, AFQ_FP16 = 1, AFQ_FP32 = 2 };
 /* RMSNorm kinds: y = n * w (standard) or y = n * (1 + w) (Gemma). */
 enum { AFQ_RMSNORM_STANDARD = 0, AFQ_RMSNORM_GEMMA = 1 };
+/* What the quantiser reads (afq_norm_desc / afq_act_desc .quant_input).
+ *   AFQ_QIN_DEFAULT  norm: the dtype-rounded normed row (every mode);
+ *                    SiLU: MXFP8 the fp32 activation, 1x128 the bf16 one
+ *   AFQ_QIN_FP32     norm, AFQ_BLOCK128 and AFQ_PER_TOKEN only: the fp32
+ *                    normed value (fp32-direct)
+ *   AFQ_QIN_BF16     SiLU, AFQ_MXFP8 only: the fp32 activation rounded to
+ *                    bf16 (bf16-first)
+ * Another value is AFQ_ERR_ARG; a value another path or mode does not
+ * offer is AFQ_ERR_UNSUPPORTED. */
+enum { AFQ_QIN_DEFAULT = 0, AFQ_QIN_FP32 = 1, AFQ_QIN_BF16 = 2 };
 
 /* Largest row width (per segment) the kernels are built for. */
 #define AFQ_MAX_COLS 32768
@@ -139,6 +162,7 @@ typedef struct afq_norm_seg {
 /*
  * fused_add_rmsnorm_quant descriptor.
  *   M            rows (>= 0)
+ *   quant_input  AFQ_QIN_DEFAULT, or AFQ_QIN_FP32 (1x128 / per-token)
  *   nseg         1, or 2 for two independent row segments normed in one
  *                launch with separate weights (the q / kv RMSNorm of MLA
  *                attention: SGLang pull request 34502, "Change", decode
@@ -160,7 +184,7 @@ typedef struct afq_norm_desc {
     int32_t dtype;
     int32_t mode;
     float eps;
-    int32_t reserved; /* must be 0 */
+    int32_t quant_input; /* AFQ_QIN_DEFAULT or AFQ_QIN_FP32 */
     const void *residual_in;
     void *residual_out;
     afq_norm_seg seg[2];
@@ -173,6 +197,7 @@ typedef struct afq_norm_desc {
  *   gate_up_row_stride  elements, >= 2I; pitch in bytes a multiple of 16
  *   mode           AFQ_MXFP8 or AFQ_BLOCK128 (AFQ_PER_TOKEN is not offered:
  *                  AFQ_ERR_UNSUPPORTED)
+ *   quant_input    AFQ_QIN_DEFAULT, or AFQ_QIN_BF16 (MXFP8)
  *   out            [M, I] codes and scales; out.normed = optional bf16 copy
  *                  of the activation a.
  */
@@ -182,7 +207,7 @@ typedef struct afq_act_desc {
     const void *gate_up;
     int64_t gate_up_row_stride;
     int32_t mode;
-    int32_t reserved; /* must be 0 */
+    int32_t quant_input; /* AFQ_QIN_DEFAULT or AFQ_QIN_BF16 */
     afq_qact out;
 } afq_act_desc;
 

@@ -51,17 +51,18 @@ def check_norm(gpu: dict, ref: dict, mode: str, dtype: str, name: str, requant=T
     return stats
 
 
-def run_norm(x, w, *, r=None, kind="gemma", mode="mx", dtype="bf16", eps=1e-6, want_normed=True):
+def run_norm(x, w, *, r=None, kind="gemma", mode="mx", dtype="bf16", eps=1e-6, want_normed=True,
+             qin=0):
     xt, wt = dev16(x, dtype), dev16(w, dtype)
     rt = dev16(r, dtype) if r is not None else None
     qa = afq.fused_add_rmsnorm_quant(xt, wt, eps, mode=MODE[mode], kind=KIND[kind], residual=rt,
-                                     want_normed=want_normed)
+                                     want_normed=want_normed, quant_input=qin)
     torch.cuda.synchronize()
     return dict(h=host16(qa.residual) if r is not None else None,
                 normed=host16(qa.normed) if want_normed else None,
                 values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
 
 
-def ref_norm(x, w, *, r=None, kind="gemma", mode="mx", dtype="bf16", eps=1e-6, rows=None):
+def ref_norm(x, w, *, r=None, kind="gemma", mode="mx", dtype="bf16", eps=1e-6, rows=None, qin=0):
     return orc.norm_quant(x, w, residual=r, kind=KIND[kind], dtype=ORC_DT[dtype], mode=MODE[mode],
-                          eps=eps, want_normed=True, threads=8, rows=rows)
+                          eps=eps, want_normed=True, threads=8, rows=rows, qin=qin)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert afq.abi_version() == 1
+    assert afq.abi_version() == 2
     for st in range(0, -9, -1):
         s = afq.status_string(st)
         assert s and s != "unknown status"
@@ -49,9 +49,9 @@ def test_descriptor_layout_matches_header(tmp_path):
     fields = {
         "afq_qact": ["values", "scales", "normed"],
         "afq_norm_seg": ["x", "x_row_stride", "weight", "cols", "out"],
-        "afq_norm_desc": ["M", "nseg", "kind", "dtype", "mode", "eps", "reserved", "residual_in",
+        "afq_norm_desc": ["M", "nseg", "kind", "dtype", "mode", "eps", "quant_input", "residual_in",
                           "residual_out", "seg"],
-        "afq_act_desc": ["M", "I", "gate_up", "gate_up_row_stride", "mode", "reserved", "out"],
+        "afq_act_desc": ["M", "I", "gate_up", "gate_up_row_stride", "mode", "quant_input", "out"],
         "afq_quant_desc": ["M", "cols", "x", "x_row_stride", "dtype", "mode", "out"],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "afq.h"', "int main(void){"]
@@ -107,7 +107,9 @@ def test_norm_validation_errors():
     assert _call_norm(_norm(dtype=2)) == -4                    # fp32 norm input
     assert _call_norm(_norm(eps=-1.0)) == -7
     assert _call_norm(_norm(eps=float("nan"))) == -7
-    assert _call_norm(_norm(reserved=1)) == -7
+    assert _call_norm(_norm(quant_input=3)) == -7              # unknown quant_input
+    assert _call_norm(_norm(quant_input=afq.QIN_FP32)) == -6   # fp32-direct: not with MXFP8
+    assert _call_norm(_norm(quant_input=afq.QIN_BF16)) == -6   # bf16-first: SiLU only
     d = _norm()
     d.seg[0].x_row_stride = 128                                # stride < cols
     assert _call_norm(d) == -2
@@ -150,6 +152,13 @@ def test_act_and_quant_validation_errors():
     assert lib.silu_mul_quant(None, None) == -1
     d.mode = afq.PER_TOKEN
     assert lib.silu_mul_quant(ctypes.byref(d), None) == -6
+    d.mode, d.quant_input = afq.MXFP8, 3
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -7     # unknown quant_input
+    d.quant_input = afq.QIN_FP32
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -6     # fp32-direct: norm only
+    d.mode, d.quant_input = afq.BLOCK128, afq.QIN_BF16
+    assert lib.silu_mul_quant(ctypes.byref(d), None) == -6     # bf16-first: MXFP8 only
+    d.quant_input = afq.QIN_DEFAULT
     d.mode = afq.BLOCK128                                       # 768 % 128 == 0 but ...
     d.I = 96
     assert lib.silu_mul_quant(ctypes.byref(d), None) == -2     # 96 % 128 != 0

@@ -466,6 +466,93 @@ def test_rejected_call_writes_nothing():
     assert bool((values.view(torch.uint8) == 7).all())
 
 
+# ------------------------------------------------- rounding-point variants
+def _exact_report(name, gpu, ref, stats):
+    stats = dict(stats)
+    stats["codes_equal"] = bool(np.array_equal(gpu["values"], ref["values"]))
+    stats["scales_equal"] = bool(np.array_equal(np.asarray(gpu["scales"]).view(np.uint8),
+                                                np.asarray(ref["scales"]).view(np.uint8)))
+    _report(name, stats)
+
+
+@pytest.mark.parametrize("mode", ["b128", "pt"])
+@pytest.mark.parametrize("kind", ["gemma", "standard"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("H,M", [(4096, 33), (2048, 5), (6144, 1100)])
+def test_norm_fp32_direct(mode, kind, dtype, H, M):
+    """fp32-direct: the quantiser reads the fp32 normed value.  The kernel
+    takes inv from an fp64 sum of squares rounded once to fp32, as the
+    oracle does, so codes and scales are expected to match it exactly; the
+    contract's budget is the pass bar."""
+    d = inputs.norm_inputs(M, H, seed=15, x_std=2.0, r_std=1.0,
+                           w_kind="uniform" if kind == "standard" else "normal",
+                           w_param=0.5 if kind == "standard" else 0.1, dtype=dtype)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind=kind, mode=mode, dtype=dtype, qin=afq.QIN_FP32)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind=kind, mode=mode, dtype=dtype, qin=orc.QIN_FP32)
+    stats = check_norm(gpu, ref, mode, dtype, "fp32-direct", requant=False)
+    _exact_report(f"fp32-direct {mode}-{kind}-{dtype} H={H} M={M}", gpu, ref, stats)
+
+
+def test_norm_fp32_direct_edge_rows_and_two_segments():
+    H = 2048
+    rows = inputs.edge_rows(H)
+    x = inputs.to_bits(rows)
+    w = inputs.to_bits(np.random.default_rng(3).uniform(0.5, 1.5, H))
+    for mode in ("b128", "pt"):
+        gpu = run_norm(x, w, kind="standard", mode=mode, qin=afq.QIN_FP32)
+        ref = ref_norm(x, w, kind="standard", mode=mode, qin=orc.QIN_FP32)
+        check_norm(gpu, ref, mode, "bf16", f"fp32-direct edge {mode}", requant=False)
+    M = 2048
+    segs = inputs.two_segment_inputs(M, (1536, 512), seed=4)
+    buf = np.zeros((M, 2112), np.uint16)
+    buf[:, :1536], buf[:, 1536:2048] = segs[0]["x"], segs[1]["x"]
+    bt = dev16(buf)
+    outs = afq.fused_add_rmsnorm_quant([bt[:, :1536], bt[:, 1536:2048]],
+                                       [dev16(segs[0]["w"]), dev16(segs[1]["w"])], 1e-6,
+                                       mode=afq.PER_TOKEN, kind=afq.STANDARD, want_normed=True,
+                                       quant_input=afq.QIN_FP32)
+    torch.cuda.synchronize()
+    for sg, qa in zip(segs, outs):
+        gpu = dict(normed=host16(qa.normed), values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
+        ref = ref_norm(sg["x"], sg["w"], kind="standard", mode="pt", qin=orc.QIN_FP32)
+        stats = check_norm(gpu, ref, "pt", "bf16", "fp32-direct two-seg", requant=False)
+        _exact_report(f"fp32-direct two-seg cols={sg['x'].shape[1]}", gpu, ref, stats)
+
+
+def test_norm_fp32_direct_prefill_sampled_rows():
+    """The 1x128 fp32-direct launch at the benchmark shape (H = 4096,
+    M = 4096), sampled rows against the oracle."""
+    M, H = 4096, 4096
+    d = inputs.norm_inputs(M, H, seed=0, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="b128", qin=afq.QIN_FP32)
+    rows = np.sort(np.random.default_rng(2).choice(M, 64, replace=False))
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="b128", rows=rows, qin=orc.QIN_FP32)
+    sub = {k: (None if v is None else v[rows]) for k, v in gpu.items()}
+    rsub = {k: (None if v is None else v[rows]) for k, v in ref.items()}
+    stats = check_norm(sub, rsub, "b128", "bf16", "fp32-direct prefill", requant=False)
+    _exact_report("fp32-direct prefill sampled", sub, rsub, stats)
+
+
+@pytest.mark.parametrize("M,I", [(8, 768), (192, 768), (64, 12288), (3, 2176)])
+def test_silu_mx_bf16_first(M, I):
+    """bf16-first MXFP8 SiLU-and-mul: the quantiser reads the bf16-rounded
+    activation.  Against the oracle within the contract, and bit for bit the
+    standalone MXFP8 quantiser applied to the kernel's own bf16 activation
+    (fused = unfused)."""
+    gu = inputs.gate_up_inputs(M, I, seed=5, std=2.0)
+    qa = afq.silu_mul_quant(dev16(gu), afq.MXFP8, want_act=True, quant_input=afq.QIN_BF16)
+    sep = afq.fp8_quant(qa.normed, afq.MXFP8)
+    torch.cuda.synchronize()
+    act, values, scales = host16(qa.normed), host8(qa.values), scales_u8_or_f32(qa.scales)
+    ref = orc.silu_quant(gu, orc.MXFP8, threads=8, qin=orc.QIN_BF16)
+    na = check_dtype16(act, ref["act"], "bf16-first act")
+    n1 = check_codes(values, ref["values"], "bf16-first codes")
+    nb = check_scales(scales, ref["scales"], 0, "bf16-first scales")
+    assert np.array_equal(values, host8(sep.values))
+    assert np.array_equal(scales, scales_u8_or_f32(sep.scales))
+    _report(f"silu-mx bf16-first M={M} I={I}", dict(act_1ulp=na, codes_1=n1, scales_bad=nb))
+
+
 # ------------------------------------------------------- full-size sampled
 def test_full_size_prefill_sampled_rows():
     """The benchmark workload (M = 16384, H = 6144, seed 1, x, r ~ N(0,3^2)),
