@@ -17,17 +17,39 @@ thread_local int g_last_hip_error = 0;
 
 struct Span {
     uintptr_t lo = 0, hi = 0; // [lo, hi), empty when lo == hi
+    bool wraps = false;       // the buffer would run past the end of the address space
 };
 
-// Byte span of a [rows, cols] array of `elt`-byte elements, row pitch in bytes.
+// Byte span of a [rows, cols] array of `elt`-byte elements, row pitch in
+// bytes (rows, cols, elt, pitch >= 0).  Computed in unsigned 64-bit with
+// overflow checks: an extent that does not fit marks the span as wrapping.
 Span span_of(const void *p, int64_t rows, int64_t cols, int64_t elt, int64_t pitch)
 {
     Span s;
     if (!p || rows <= 0 || cols <= 0) return s;
+    uint64_t body, last, len, end;
+    if (__builtin_mul_overflow((uint64_t)(rows - 1), (uint64_t)pitch, &body) ||
+        __builtin_mul_overflow((uint64_t)cols, (uint64_t)elt, &last) ||
+        __builtin_add_overflow(body, last, &len) ||
+        __builtin_add_overflow((uint64_t)(uintptr_t)p, len, &end)) {
+        s.wraps = true;
+        return s;
+    }
     s.lo = (uintptr_t)p;
-    s.hi = s.lo + (uintptr_t)((rows - 1) * pitch + cols * elt);
+    s.hi = (uintptr_t)end;
     return s;
 }
+
+bool any_wraps(const Span *a, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (a[i].wraps) return true;
+    return false;
+}
+
+// Row count and row stride bounds shared by every entry point.
+bool rows_ok(int64_t M) { return M >= 0 && M <= AFQ_MAX_ROWS; }
+bool stride_ok(int64_t stride, int64_t min) { return stride >= min && stride <= AFQ_MAX_ROW_STRIDE; }
 
 bool overlap(const Span &a, const Span &b)
 {
@@ -87,7 +109,7 @@ const char *afq_status_string(int status)
     switch (status) {
     case AFQ_OK: return "ok";
     case AFQ_ERR_NULL: return "a required pointer is NULL";
-    case AFQ_ERR_SHAPE: return "invalid shape (M, width, group multiple, row stride or segment count)";
+    case AFQ_ERR_SHAPE: return "invalid shape (M, width, group multiple, row stride, buffer extent or segment count)";
     case AFQ_ERR_ALIGN: return "pointer or row pitch not aligned (16 bytes; scales 4 bytes)";
     case AFQ_ERR_DTYPE: return "dtype not supported by this entry point";
     case AFQ_ERR_ALIAS: return "an output overlaps another output or an input";
@@ -110,14 +132,14 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
     if (!(std::isfinite(d->eps) && d->eps >= 0.0f)) return AFQ_ERR_ARG;
     if (d->quant_input == AFQ_QIN_BF16) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_FP32 && d->mode == AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
-    if (d->M < 0) return AFQ_ERR_SHAPE;
+    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
     if (d->nseg != 1 && d->nseg != 2) return AFQ_ERR_SHAPE;
     const bool has_res = d->residual_in != nullptr || d->residual_out != nullptr;
     if (has_res && d->nseg != 1) return AFQ_ERR_SHAPE;
     for (int s = 0; s < d->nseg; ++s) {
         const afq_norm_seg &g = d->seg[s];
         if (!width_ok(g.cols, d->mode)) return AFQ_ERR_SHAPE;
-        if (g.x_row_stride < g.cols) return AFQ_ERR_SHAPE;
+        if (!stride_ok(g.x_row_stride, g.cols)) return AFQ_ERR_SHAPE;
     }
     if (d->nseg == 2 && (d->seg[0].cols + d->seg[1].cols) > AFQ_MAX_COLS) return AFQ_ERR_SHAPE;
     if (d->M == 0) return AFQ_OK;
@@ -152,10 +174,12 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
         ins[ni++] = span_of(g.x, M, g.cols, elt, g.x_row_stride * elt);
         ins[ni++] = span_of(g.weight, 1, g.cols, elt, g.cols * elt);
     }
+    if (any_wraps(outs, no) || any_wraps(ins, ni)) return AFQ_ERR_SHAPE;
     if (has_res) {
         const int64_t c = d->seg[0].cols;
         const Span rout = span_of(d->residual_out, M, c, elt, c * elt);
         const Span rin = span_of(d->residual_in, M, c, elt, c * elt);
+        if (rout.wraps || rin.wraps) return AFQ_ERR_SHAPE;
         // residual_out may only coincide exactly with residual_in
         if (d->residual_out != d->residual_in && overlap(rout, rin)) return AFQ_ERR_ALIAS;
         if (any_overlap(outs, no, ins, ni)) return AFQ_ERR_ALIAS;
@@ -199,9 +223,9 @@ int silu_mul_quant(const afq_act_desc *d, void *stream)
     if (d->mode == AFQ_PER_TOKEN) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_FP32) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_BF16 && d->mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
-    if (d->M < 0) return AFQ_ERR_SHAPE;
+    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
     if (!width_ok(d->I, d->mode)) return AFQ_ERR_SHAPE;
-    if (d->gate_up_row_stride < 2 * d->I) return AFQ_ERR_SHAPE;
+    if (!stride_ok(d->gate_up_row_stride, 2 * d->I)) return AFQ_ERR_SHAPE;
     if (d->M == 0) return AFQ_OK;
     if (!d->gate_up || !d->out.values || !d->out.scales) return AFQ_ERR_NULL;
     if (!aligned(d->gate_up, 16) || (d->gate_up_row_stride * 2) % 16 != 0) return AFQ_ERR_ALIGN;
@@ -216,6 +240,7 @@ int silu_mul_quant(const afq_act_desc *d, void *stream)
         span_of(d->out.normed, M, I, 2, I * 2),
     };
     Span ins[1] = {span_of(d->gate_up, M, 2 * I, 2, d->gate_up_row_stride * 2)};
+    if (any_wraps(outs, 3) || any_wraps(ins, 1)) return AFQ_ERR_SHAPE;
     if (any_overlap(outs, 3, ins, 1)) return AFQ_ERR_ALIAS;
 
     afq::ActPlan p{};
@@ -236,9 +261,9 @@ int fp8_quant(const afq_quant_desc *d, void *stream)
     if (!d) return AFQ_ERR_NULL;
     if (!valid_mode(d->mode)) return AFQ_ERR_ARG;
     if (d->dtype != AFQ_BF16 && d->dtype != AFQ_FP16 && d->dtype != AFQ_FP32) return AFQ_ERR_ARG;
-    if (d->M < 0) return AFQ_ERR_SHAPE;
+    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
     if (!width_ok(d->cols, d->mode)) return AFQ_ERR_SHAPE;
-    if (d->x_row_stride < d->cols) return AFQ_ERR_SHAPE;
+    if (!stride_ok(d->x_row_stride, d->cols)) return AFQ_ERR_SHAPE;
     if (d->M == 0) return AFQ_OK;
     if (!d->x || !d->out.values || !d->out.scales) return AFQ_ERR_NULL;
     if (d->out.normed) return AFQ_ERR_ARG;
@@ -253,6 +278,7 @@ int fp8_quant(const afq_quant_desc *d, void *stream)
                 scale_cols(d->mode, n) * scale_elt(d->mode)),
     };
     Span ins[1] = {span_of(d->x, M, n, elt, d->x_row_stride * elt)};
+    if (any_wraps(outs, 2) || any_wraps(ins, 1)) return AFQ_ERR_SHAPE;
     if (any_overlap(outs, 2, ins, 1)) return AFQ_ERR_ALIAS;
 
     afq::QuantPlan p{};

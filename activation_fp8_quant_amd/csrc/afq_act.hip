@@ -212,7 +212,7 @@ int launch_act(const ActPlan &p, void *stream)
         a.gu = p.gu + r0 * p.gu_pitch;
         a.gu_pitch = p.gu_pitch;
         a.values = p.values + r0 * p.I;
-        a.scales = p.scales + r0 * (p.mode == kMX ? p.I / 32 : 4 * (p.I / 128));
+        a.scales = p.scales + r0 * scale_row_bytes(p.mode, p.I);
         a.act = p.act ? p.act + r0 * p.I * 2 : nullptr;
         a.C = C;
         a.I = p.I;

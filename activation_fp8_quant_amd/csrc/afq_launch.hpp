@@ -62,4 +62,19 @@ static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
 // 2^31 (larger M is covered by several launches over row slices).
 static inline int64_t flat_rows_per_launch(int32_t C) { return ((int64_t)1 << 31) / C; }
 
+// Rows per launch of the row kernels (NT lanes per row, R rows per block):
+// a launch stays below 2^31 work-items (a dispatch's grid size is a 32-bit
+// count of work-items), a whole number of blocks; larger M is covered by
+// several launches over row slices.
+static inline int64_t row_rows_per_launch(int NT, int R)
+{
+    return (((int64_t)1 << 31) / NT) / R * R;
+}
+
+// Bytes of scales per row of `cols` elements in quant mode `mode`.
+static inline int64_t scale_row_bytes(int mode, int32_t cols)
+{
+    return mode == kMX ? cols / 32 : mode == kB128 ? 4 * (cols / 128) : 4;
+}
+
 } // namespace afq

@@ -353,9 +353,25 @@ int launch_norm(const NormPlan &p, void *stream)
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
     const bool f32q = p.qin == 1;
-    hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(a, p.mode, f32q, gemma, p.nseg, sh.CPL, st)
-                                    : go_norm_mode<kBF16>(a, p.mode, f32q, gemma, p.nseg, sh.CPL, st);
-    return (int)e;
+    // one launch per row slice (a single one below ~2^31 / NT rows)
+    const int64_t step = row_rows_per_launch(a.NT, a.R);
+    NormArgs b = a;
+    for (int64_t r0 = 0; r0 < p.M; r0 += step) {
+        b.M = p.M - r0 < step ? p.M - r0 : step;
+        for (int s = 0; s < 2; ++s) {
+            const NormSegPlan &g = a.seg[s];
+            b.seg[s].x = g.x + r0 * g.x_pitch;
+            b.seg[s].values = g.values + r0 * g.cols;
+            b.seg[s].scales = g.scales + r0 * scale_row_bytes(p.mode, g.cols);
+            b.seg[s].normed = g.normed ? g.normed + r0 * g.cols * 2 : nullptr;
+        }
+        b.res_in = a.res_in ? a.res_in + r0 * a.C0 * 16 : nullptr;
+        b.res_out = a.res_out ? a.res_out + r0 * a.C0 * 16 : nullptr;
+        const hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(b, p.mode, f32q, gemma, p.nseg, sh.CPL, st)
+                                              : go_norm_mode<kBF16>(b, p.mode, f32q, gemma, p.nseg, sh.CPL, st);
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
 }
 
 } // namespace afq

@@ -145,17 +145,29 @@ static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
         a.NT = sh.NT;
         a.R = sh.R;
         a.WPR = sh.WPR;
-        switch (sh.CPL) {
-        case 1: return go_quant_row<DT, 1>(a, st);
-        case 2: return go_quant_row<DT, 2>(a, st);
-        case 3: return go_quant_row<DT, 3>(a, st);
-        default: return go_quant_row<DT, 4>(a, st);
+        // one launch per row slice (a single one below ~2^31 / NT rows)
+        const int64_t step = row_rows_per_launch(a.NT, a.R);
+        QuantArgs b = a;
+        for (int64_t r0 = 0; r0 < a.M; r0 += step) {
+            b.M = a.M - r0 < step ? a.M - r0 : step;
+            b.x = a.x + r0 * a.x_pitch;
+            b.values = a.values + r0 * a.cols;
+            b.scales = a.scales + r0 * 4;
+            hipError_t e;
+            switch (sh.CPL) {
+            case 1: e = go_quant_row<DT, 1>(b, st); break;
+            case 2: e = go_quant_row<DT, 2>(b, st); break;
+            case 3: e = go_quant_row<DT, 3>(b, st); break;
+            default: e = go_quant_row<DT, 4>(b, st); break;
+            }
+            if (e != hipSuccess) return e;
         }
+        return hipSuccess;
     }
     // flat kernels over row slices of at most 2^31 chunks
     constexpr int EB = DT == kFP32 ? 4 : 2;
     const int64_t step = flat_rows_per_launch(a.C);
-    const int64_t sbytes = mode == kMX ? a.cols / 32 : 4 * (a.cols / 128);
+    const int64_t sbytes = scale_row_bytes(mode, a.cols);
     QuantArgs b = a;
     b.dc = divc((uint32_t)a.C);
     for (int64_t r0 = 0; r0 < a.M; r0 += step) {

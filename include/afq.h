@@ -97,10 +97,12 @@ extern "C" {
 enum {
     AFQ_OK = 0,
     AFQ_ERR_NULL = -1,        /* a required pointer (or the descriptor) is NULL */
-    AFQ_ERR_SHAPE = -2,       /* M < 0, cols/I not a positive multiple of the group
-                                 size and of 8, cols above AFQ_MAX_COLS, row stride
-                                 smaller than the row, nseg not 1 or 2, or a
-                                 residual with two segments */
+    AFQ_ERR_SHAPE = -2,       /* M < 0 or above AFQ_MAX_ROWS, cols/I not a positive
+                                 multiple of the group size and of 8, cols above
+                                 AFQ_MAX_COLS, row stride smaller than the row or
+                                 above AFQ_MAX_ROW_STRIDE, a buffer that would run
+                                 past the end of the address space, nseg not 1 or 2,
+                                 or a residual with two segments */
     AFQ_ERR_ALIGN = -3,       /* a base pointer or row pitch not 16-byte aligned
                                  (scales: 4-byte aligned) */
     AFQ_ERR_DTYPE = -4,       /* dtype not allowed for this entry point */
@@ -132,6 +134,11 @@ enum { AFQ_QIN_DEFAULT = 0, AFQ_QIN_FP32 = 1, AFQ_QIN_BF16 = 2 };
 
 /* Largest row width (per segment) the kernels are built for. */
 #define AFQ_MAX_COLS 32768
+/* Largest row count of one call (the row kernels launch up to one
+ * workgroup per row). */
+#define AFQ_MAX_ROWS 2147483647
+/* Largest row stride, in elements. */
+#define AFQ_MAX_ROW_STRIDE ((int64_t)1 << 40)
 
 /*
  * A quantised activation (the tuple a quantised linear consumes: codes,

@@ -107,6 +107,13 @@ def test_norm_validation_errors():
     assert _call_norm(_norm(dtype=2)) == -4                    # fp32 norm input
     assert _call_norm(_norm(eps=-1.0)) == -7
     assert _call_norm(_norm(eps=float("nan"))) == -7
+    assert _call_norm(_norm(M=2 ** 31)) == -2                  # above AFQ_MAX_ROWS
+    d = _norm()
+    d.seg[0].x_row_stride = 2 ** 40 + 256                      # above AFQ_MAX_ROW_STRIDE
+    assert _call_norm(d) == -2
+    d = _norm(M=1 << 20)
+    d.seg[0].out.values = (1 << 64) - (1 << 24)                # would run past the address space
+    assert _call_norm(d) == -2
     assert _call_norm(_norm(quant_input=3)) == -7              # unknown quant_input
     assert _call_norm(_norm(quant_input=afq.QIN_FP32)) == -6   # fp32-direct: not with MXFP8
     assert _call_norm(_norm(quant_input=afq.QIN_BF16)) == -6   # bf16-first: SiLU only

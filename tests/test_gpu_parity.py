@@ -553,6 +553,36 @@ def test_silu_mx_bf16_first(M, I):
     _report(f"silu-mx bf16-first M={M} I={I}", dict(act_1ulp=na, codes_1=n1, scales_bad=nb))
 
 
+# ------------------------------------------------------ split launches
+def test_row_kernels_split_large_launches():
+    """A row-kernel launch stays below 2^31 work-items: 8-column per-token
+    rows take 64 lanes each, so more than 2^25 rows take two launches.  Rows
+    on both sides of the split, against the oracle, for the fused norm and
+    the standalone per-token quantiser."""
+    M, H = (1 << 25) + 1000, 8
+    base = inputs.norm_inputs(4096, H, seed=16, x_std=1.0, r_std=None, w_kind="uniform", w_param=0.5)
+    x = np.tile(base["x"], (M // 4096 + 1, 1))[:M]
+    xt = dev16(x)
+    qa = afq.fused_add_rmsnorm_quant(xt, dev16(base["w"]), 1e-6, mode=afq.PER_TOKEN,
+                                     kind=afq.STANDARD)
+    sep = afq.fp8_quant(xt, afq.PER_TOKEN)
+    torch.cuda.synchronize()
+    edge = [0, 1, (1 << 25) - 2, (1 << 25) - 1, 1 << 25, (1 << 25) + 1, M - 2, M - 1]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(3).choice(M, 56, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    pick8 = lambda t: t.view(torch.uint8)[idx].cpu().numpy()
+    pickf = lambda t: t[idx].cpu().numpy()
+    ref = orc.norm_quant(x[rows], base["w"], kind=orc.STANDARD, dtype=orc.BF16, mode=orc.PER_TOKEN,
+                         eps=1e-6)
+    check_codes(pick8(qa.values), ref["values"], "split norm codes")
+    check_scales(pickf(qa.scales), ref["scales"], 2, "split norm scales")
+    q, s = orc.quant(x[rows], orc.BF16, orc.PER_TOKEN)
+    assert np.array_equal(pick8(sep.values), q)
+    assert np.array_equal(pickf(sep.scales).view(np.uint32), s.view(np.uint32))
+    del xt, qa, sep
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- full-size sampled
 def test_full_size_prefill_sampled_rows():
     """The benchmark workload (M = 16384, H = 6144, seed 1, x, r ~ N(0,3^2)),
