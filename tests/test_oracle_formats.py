@@ -157,3 +157,35 @@ def test_e8m0_brute_force_smallest_scale():
         assert orc.lib().orc_e8m0_byte(a) == b, a
         if b > 0:
             assert 256 <= Fraction(a) / Fraction(2) ** (b - 127) < 512
+
+
+def test_mx_quant_every_bf16_value_under_every_block_exponent():
+    """The MXFP8 block quantiser over every finite bf16 value u under every
+    block exponent that admits it.  A block's amax is the largest bf16 of
+    fp32 exponent field E (E = 1..254), so every u of exponent field <= E
+    fits under it; the scale byte must be max(E - 8, 0) and each code
+    e4m3(clamp(u 2^(127-b), +-448)), checked against torch's float8_e4m3fn
+    cast of the exactly scaled value (fp64 scaling is exact; the result is
+    exact in fp32 wherever it can reach an e4m3 rounding boundary)."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    fin = c[((c >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    field = (fin.astype(np.uint32) >> 7) & 0xFF
+    rows, bytes_exp = [], []
+    for E in range(1, 255):
+        vals = fin[field <= E]
+        amax = np.uint16((E << 7) | 0x7F)
+        n = -(-vals.size // 31)
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:vals.size] = vals
+        blk = np.concatenate([np.full((n, 1), amax, np.uint16), pad.reshape(n, 31)], axis=1)
+        rows.append(blk)
+        bytes_exp.append(np.full(n, max(E - 8, 0), np.uint8))
+    x = np.concatenate(rows)
+    want_b = np.concatenate(bytes_exp)
+    codes, scales = orc.quant(x, orc.BF16, orc.MXFP8, threads=8)
+    assert np.array_equal(scales[:, 0], want_b)
+    u = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy()
+    v = np.clip(np.ldexp(u, (127 - want_b.astype(np.int64))[:, None]), -448.0, 448.0)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.argwhere(codes != ref)
+    assert bad.size == 0, (bad[:5].tolist(), x[tuple(bad[0])] if bad.size else None)
