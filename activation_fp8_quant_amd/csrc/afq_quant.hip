@@ -85,7 +85,8 @@ quant_row_kernel(const QuantArgs a)
 {
     constexpr int EB = DT == kFP32 ? 4 : 2;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // rows are whole wavefronts: the wavefront and its row are uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rib = wave / a.WPR;
     const int t = tid - rib * a.NT;
     const int64_t row = (int64_t)blockIdx.x * a.R + rib;
@@ -165,7 +166,6 @@ static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
         return hipSuccess;
     }
     // flat kernels over row slices of at most 2^31 chunks
-    constexpr int EB = DT == kFP32 ? 4 : 2;
     const int64_t step = flat_rows_per_launch(a.C);
     const int64_t sbytes = scale_row_bytes(mode, a.cols);
     QuantArgs b = a;
@@ -180,7 +180,6 @@ static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
         const hipError_t e = mode == kMX ? go_quant_flat<DT, kMX, 1>(b, st) : go_quant_flat<DT, kB128, 1>(b, st);
         if (e != hipSuccess) return e;
     }
-    (void)EB;
     return hipSuccess;
 }
 
