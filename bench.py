@@ -26,8 +26,9 @@ Also reported, in the same JSON line:
   cpu_baseline the CPU oracle on a bounded sample of the headline workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu]
-    python bench.py --profile    (only the headline kernel and a 1 GiB copy,
-                                  for rocprofv3 counter runs)
+    python bench.py --profile [NAME]   (one workload -- the headline, or one of
+                                        PROFILE_WORKLOADS -- and a 1 GiB copy,
+                                        for rocprofv3 trace and counter runs)
 """
 from __future__ import annotations
 
@@ -377,6 +378,30 @@ def run_sweep():
     return out
 
 
+# Workloads of `--profile NAME` (besides the headline): the rotated bench
+# workloads, built exactly as the sweep builds them.
+def _prof_norm_b128(qin=0):
+    import activation_fp8_quant_amd as afq
+    ws = norm_bytes(4096, 4096, normed=False, mode="b128")
+    return NormCase(4096, 4096, seed=0, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5,
+                    kind="standard", mode="b128", normed=False, sets=rotation_sets(ws),
+                    qin=afq.QIN_FP32 if qin else 0)
+
+
+PROFILE_WORKLOADS = {
+    "norm_mx_m4096": lambda: NormCase(4096, 6144, seed=1, x_std=3.0, r_std=3.0, w_kind="normal",
+                                      w_param=0.1, kind="gemma", mode="mx",
+                                      sets=rotation_sets(norm_bytes(4096, 6144))),
+    "norm_b128_h4096": lambda: _prof_norm_b128(),
+    "norm_b128_f32q_h4096": lambda: _prof_norm_b128(qin=1),
+    "twoseg_pt_m8192": lambda: TwoSegCase(8192, seed=0, sets=rotation_sets(two_seg_bytes(8192))),
+    "silu_b128_i12288": lambda: SiluCase(4096, 12288, seed=0, std=1.0, mode="b128",
+                                         sets=rotation_sets(silu_bytes(4096, 12288, mode="b128"))),
+    "silu_b128_i3072": lambda: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128",
+                                        sets=rotation_sets(silu_bytes(16384, 3072, mode="b128"))),
+}
+
+
 # ----------------------------------------------------------------- CPU leg
 def cpu_baseline(rows=16384):
     """The oracle, as it stands, on a bounded sample of the headline
@@ -415,8 +440,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--profile", action="store_true",
-                    help="only the headline kernel and a 1 GiB device copy (counter runs)")
+    ap.add_argument("--profile", nargs="?", const="headline", default=None,
+                    choices=["headline"] + sorted(PROFILE_WORKLOADS),
+                    help="only one workload (default: the headline) and a 1 GiB device copy "
+                         "(for rocprofv3 trace and counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused kernels are row-independent and this build "
@@ -435,14 +462,20 @@ def main():
     print(f"[bench] headline inputs ready ({head.bytes / 1e6:.1f} MB per launch)", file=sys.stderr, flush=True)
 
     if args.profile:
+        work = head
+        if args.profile != "headline":
+            del head
+            torch.cuda.empty_cache()
+            work = PROFILE_WORKLOADS[args.profile]()
         for _ in range(args.warmup + args.steps):
-            head()
+            work()
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": True, "steps": args.steps, "copy_bytes": 1 << 30}), flush=True)
+        print(json.dumps({"profile": args.profile, "steps": args.steps, "warmup": args.warmup,
+                          "bytes_per_launch": work.bytes, "copy_bytes": 1 << 30}), flush=True)
         return
 
     torch.cuda.synchronize()
