@@ -217,6 +217,55 @@ __device__ __forceinline__ double sum_wave_f64(double v)
 }
 __device__ __forceinline__ float max_wave(float v) { return max_xor32(max_xor16(max_row16(v))); }
 
+// Cross-wavefront step of a row reduction.  Each of the row's n <= 16
+// wavefronts has left its partial in LDS: p0[0..n) (and p1[0..n) for a
+// second segment).  Lane i < n of the first DPP row reads p0[i], lane
+// 16 + i reads p1[i], every other lane takes the identity; one 16-lane
+// reduction per DPP row then leaves each row's total in all of its lanes,
+// and lanes 0 and 16 hand the totals out as wavefront-uniform values.  All
+// partials are read in one LDS access.
+__device__ __forceinline__ float lane_pick(float v, int lane)
+{
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lane));
+}
+template <int NSEG>
+__device__ __forceinline__ float lds_rows_sum(const float *p0, const float *p1, int n, float &t1)
+{
+    const int l = threadIdx.x & 63, i = l & 15;
+    float v = 0.f;
+    if (l < 16 * NSEG && i < n) v = (l & 16) ? p1[i] : p0[i];
+    v = sum_row16(v);
+    t1 = NSEG > 1 ? lane_pick(v, 16) : 0.f;
+    return lane_pick(v, 0);
+}
+// the same for the largest of non-negative partials
+template <int NSEG>
+__device__ __forceinline__ float lds_rows_max(const float *p0, const float *p1, int n, float &t1)
+{
+    const int l = threadIdx.x & 63, i = l & 15;
+    float v = 0.f;
+    if (l < 16 * NSEG && i < n) v = (l & 16) ? p1[i] : p0[i];
+    v = max_row16(v);
+    t1 = NSEG > 1 ? lane_pick(v, 16) : 0.f;
+    return lane_pick(v, 0);
+}
+// the same for fp64 partials (the 16-lane steps of sum_wave_f64)
+template <int NSEG>
+__device__ __forceinline__ double lds_rows_sum_f64(const double *p0, const double *p1, int n, double &t1)
+{
+    const int l = threadIdx.x & 63, i = l & 15;
+    double v = 0.0;
+    if (l < 16 * NSEG && i < n) v = (l & 16) ? p1[i] : p0[i];
+    v += dppd<kQuadSwap1>(v);
+    v += dppd<kQuadSwap2>(v);
+    v += dppd<kRowHalfMirror>(v);
+    v += dppd<kRowMirror>(v);
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+    t1 = NSEG > 1 ? join64(__builtin_amdgcn_readlane(lo, 16), __builtin_amdgcn_readlane(hi, 16)) : 0.0;
+    return join64(__builtin_amdgcn_readlane(lo, 0), __builtin_amdgcn_readlane(hi, 0));
+}
+
 // Block barrier that orders only LDS: the waves exchange reduction
 // partials through LDS, and their outstanding global stores need not
 // complete before the barrier (a __syncthreads() would wait for them).

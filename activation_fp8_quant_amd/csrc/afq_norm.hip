@@ -156,45 +156,37 @@ norm_quant_kernel(const NormArgs a)
 
     // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
     //      across the wavefronts of the row
-    __shared__ float redm[kMaxBlock / 64][2];
+    // (LDS partials are segment-major: a row's partials are contiguous)
+    const int p0 = rib * a.WPR;
+    __shared__ float redm[2][kMaxBlock / 64];
     float inv0, inv1;
     if constexpr (F32Q) {
-        __shared__ double redd[kMaxBlock / 64][2];
+        __shared__ double redd[2][kMaxBlock / 64];
         if (has0) sd0 = sum_wave_f64(sd0);
         if constexpr (NSEG > 1)
             if (has1) sd1 = sum_wave_f64(sd1);
         if (a.WPR > 1) {
             if ((tid & 63) == 0) {
-                redd[wave][0] = sd0;
-                if constexpr (NSEG > 1) redd[wave][1] = sd1;
+                redd[0][wave] = sd0;
+                if constexpr (NSEG > 1) redd[1][wave] = sd1;
             }
             lds_barrier();
-            sd0 = 0.0;
-            sd1 = 0.0;
-            for (int i = 0; i < a.WPR; ++i) {
-                sd0 += redd[rib * a.WPR + i][0];
-                if constexpr (NSEG > 1) sd1 += redd[rib * a.WPR + i][1];
-            }
+            sd0 = lds_rows_sum_f64<NSEG>(&redd[0][p0], &redd[1][p0], a.WPR, sd1);
         }
         inv0 = (float)(1.0 / sqrt(sd0 / (double)a.seg[0].cols + (double)a.eps));
         inv1 = NSEG > 1 ? (float)(1.0 / sqrt(sd1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
     } else {
-        __shared__ float red[kMaxBlock / 64][2];
+        __shared__ float red[2][kMaxBlock / 64];
         if (has0) ss0 = sum_wave(ss0);
         if constexpr (NSEG > 1)
             if (has1) ss1 = sum_wave(ss1);
         if (a.WPR > 1) {
             if ((tid & 63) == 0) {
-                red[wave][0] = ss0;
-                if constexpr (NSEG > 1) red[wave][1] = ss1;
+                red[0][wave] = ss0;
+                if constexpr (NSEG > 1) red[1][wave] = ss1;
             }
             lds_barrier();
-            ss0 = 0.f;
-            ss1 = 0.f;
-            for (int i = 0; i < a.WPR; ++i) {
-                ss0 += red[rib * a.WPR + i][0];
-                if constexpr (NSEG > 1) ss1 += red[rib * a.WPR + i][1];
-            }
+            ss0 = lds_rows_sum<NSEG>(&red[0][p0], &red[1][p0], a.WPR, ss1);
         }
         inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
         inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
@@ -240,16 +232,11 @@ norm_quant_kernel(const NormArgs a)
             if (has1) am1 = max_wave(am1);
         if (a.WPR > 1) {
             if ((tid & 63) == 0) {
-                redm[wave][0] = am0;
-                if constexpr (NSEG > 1) redm[wave][1] = am1;
+                redm[0][wave] = am0;
+                if constexpr (NSEG > 1) redm[1][wave] = am1;
             }
             lds_barrier();
-            am0 = 0.f;
-            am1 = 0.f;
-            for (int i = 0; i < a.WPR; ++i) {
-                am0 = __builtin_fmaxf(am0, redm[rib * a.WPR + i][0]);
-                if constexpr (NSEG > 1) am1 = __builtin_fmaxf(am1, redm[rib * a.WPR + i][1]);
-            }
+            am0 = lds_rows_max<NSEG>(&redm[0][p0], &redm[1][p0], a.WPR, am1);
         }
         const Fp32Scale sc0 = fp32_scale(am0);
         const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;

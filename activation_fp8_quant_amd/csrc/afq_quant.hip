@@ -108,8 +108,8 @@ quant_row_kernel(const QuantArgs a)
     if (a.WPR > 1) {
         if ((tid & 63) == 0) redm[wave] = am;
         lds_barrier();
-        am = 0.f;
-        for (int i = 0; i < a.WPR; ++i) am = __builtin_fmaxf(am, redm[rib * a.WPR + i]);
+        float unused;
+        am = lds_rows_max<1>(&redm[rib * a.WPR], &redm[rib * a.WPR], a.WPR, unused);
     }
     const Fp32Scale sc = fp32_scale(am);
 #pragma unroll
