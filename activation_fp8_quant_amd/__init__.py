@@ -202,14 +202,51 @@ def _rowmajor(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a device tensor")
 
 
-def _alloc_out(mode, M, cols, device, normed_dtype, out):
-    if out is not None:
-        return out
+def _same_device(t: torch.Tensor, device: torch.device, name: str):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+
+
+def _check_buf(t: torch.Tensor, numel: int, dtypes, device: torch.device, name: str):
+    """A caller-supplied output: contiguous, on the inputs' device, of an
+    accepted dtype and exactly the element count the kernel writes (the
+    library takes raw pointers and cannot check extents itself)."""
+    _same_device(t, device, name)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous tensor of {numel} elements "
+                         f"(got shape {tuple(t.shape)}, contiguous={t.is_contiguous()})")
+
+
+_CODE_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _alloc_out(mode, M, cols, device, normed_dtype, want, out):
     sshape, sdtype = _scales_shape(mode, M, cols)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be a (values, scales, normed) tuple")
+        values, scales, normed = out
+        _check_buf(values, M * cols, _CODE_DTYPES, device, "out values")
+        _check_buf(scales, sshape[0] * sshape[1], (sdtype,), device, "out scales")
+        if normed is not None:
+            _check_buf(normed, M * cols, (normed_dtype,), device, "out normed")
+        return values, scales, normed
     values = torch.empty((M, cols), dtype=torch.float8_e4m3fn, device=device)
     scales = torch.empty(sshape, dtype=sdtype, device=device)
-    normed = torch.empty((M, cols), dtype=normed_dtype, device=device) if normed_dtype else None
+    normed = torch.empty((M, cols), dtype=normed_dtype, device=device) if want else None
     return values, scales, normed
+
+
+def _launch(fn, desc, stream, device: torch.device) -> int:
+    """Call an entry point with the tensors' device current (HIP launches
+    on the current device)."""
+    arg = ctypes.c_void_p(_stream(stream, device))
+    if device.index is not None and device.index != torch.cuda.current_device():
+        with torch.cuda.device(device):
+            return fn(ctypes.byref(desc), arg)
+    return fn(ctypes.byref(desc), arg)
 
 
 # ------------------------------------------------------------- entry points
@@ -256,6 +293,8 @@ def fused_add_rmsnorm_quant(
     if dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("norm inputs must be bfloat16 or float16")
     M = xs[0].shape[0]
+    _rowmajor(xs[0], "x")
+    device = xs[0].device
     d = _NormDesc()
     d.M, d.nseg, d.kind, d.dtype, d.mode = M, len(xs), kind, _DTYPE_TAG[dtype], mode
     d.eps = float(eps)
@@ -263,13 +302,14 @@ def fused_add_rmsnorm_quant(
     results = []
     for i, (xi, wi) in enumerate(zip(xs, ws)):
         _rowmajor(xi, "x")
+        _same_device(xi, device, "x")
+        _same_device(wi, device, "weight")
         if xi.dtype != dtype or wi.dtype != dtype or xi.shape[0] != M:
             raise ValueError("segments must share dtype and row count")
         if wi.dim() != 1 or wi.shape[0] != xi.shape[1] or not wi.is_contiguous():
             raise ValueError("weight must be a contiguous [cols] tensor")
         cols = xi.shape[1]
-        values, scales, normed = _alloc_out(mode, M, cols, xi.device,
-                                            dtype if want_normed else None, outs[i])
+        values, scales, normed = _alloc_out(mode, M, cols, device, dtype, want_normed, outs[i])
         seg = d.seg[i]
         seg.x, seg.x_row_stride, seg.weight, seg.cols = xi.data_ptr(), xi.stride(0), wi.data_ptr(), cols
         seg.out.values, seg.out.scales, seg.out.normed = _ptr(values), _ptr(scales), _ptr(normed)
@@ -278,13 +318,18 @@ def fused_add_rmsnorm_quant(
         if len(xs) != 1:
             raise ValueError("a residual is only supported with one segment")
         _rowmajor(residual, "residual")
+        _same_device(residual, device, "residual")
         if not residual.is_contiguous() or residual.dtype != dtype or residual.shape != xs[0].shape:
             raise ValueError("residual must be a contiguous tensor shaped and typed like x")
         if residual_out is None:
             residual_out = residual if inplace else torch.empty_like(residual)
+        else:
+            _check_buf(residual_out, residual.numel(), (dtype,), device, "residual_out")
         d.residual_in, d.residual_out = residual.data_ptr(), residual_out.data_ptr()
         results[0].residual = residual_out
-    st = lib.fused_add_rmsnorm_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, xs[0].device)))
+    elif residual_out is not None:
+        raise ValueError("residual_out needs a residual")
+    st = _launch(lib.fused_add_rmsnorm_quant, d, stream, device)
     if st != 0:
         raise AfqError(st, "fused_add_rmsnorm_quant")
     return results[0] if len(results) == 1 else results
@@ -308,13 +353,12 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
     if two_i % 2:
         raise ValueError("gate_up must have an even number of columns")
     I = two_i // 2
-    values, scales, act = _alloc_out(mode, M, I, gate_up.device,
-                                     torch.bfloat16 if want_act else None, out)
+    values, scales, act = _alloc_out(mode, M, I, gate_up.device, torch.bfloat16, want_act, out)
     d = _ActDesc()
     d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
     d.quant_input = int(quant_input)
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
-    st = lib.silu_mul_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, gate_up.device)))
+    st = _launch(lib.silu_mul_quant, d, stream, gate_up.device)
     if st != 0:
         raise AfqError(st, "silu_mul_quant")
     return QuantizedActivation(values, scales, act, None, mode, gate_up.dtype, (M, I))
@@ -328,12 +372,14 @@ def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> Quantize
     if x.dtype not in _DTYPE_TAG:
         raise TypeError("x must be bfloat16, float16 or float32")
     M, cols = x.shape
-    values, scales, _ = _alloc_out(mode, M, cols, x.device, None, out)
+    if out is not None and out[2] is not None:
+        raise ValueError("fp8_quant writes no rounded copy: out[2] must be None")
+    values, scales, _ = _alloc_out(mode, M, cols, x.device, None, False, out)
     d = _QuantDesc()
     d.M, d.cols, d.x, d.x_row_stride = M, cols, x.data_ptr(), x.stride(0)
     d.dtype, d.mode = _DTYPE_TAG[x.dtype], mode
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), None
-    st = lib.fp8_quant(ctypes.byref(d), ctypes.c_void_p(_stream(stream, x.device)))
+    st = _launch(lib.fp8_quant, d, stream, x.device)
     if st != 0:
         raise AfqError(st, "fp8_quant")
     return QuantizedActivation(values, scales, None, None, mode, x.dtype, (M, cols))

@@ -490,11 +490,50 @@ def test_rejected_call_writes_nothing():
     values = torch.full((M, H), 7, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
     scales = torch.full((M, H // 32), 9, dtype=torch.uint8, device="cuda")
     with pytest.raises(afq.AfqError) as e:
-        # scales overlapping the codes: an alias error, detected on the host
-        afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=afq.MXFP8, out=(values, values.view(torch.uint8)[:, :8], None))
+        # scales overlapping the codes: an alias error, detected by the library
+        overlapping = values.view(torch.uint8).view(-1)[: M * (H // 32)].view(M, H // 32)
+        afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=afq.MXFP8, out=(values, overlapping, None))
     assert e.value.status == -5
     torch.cuda.synchronize()
     assert bool((values.view(torch.uint8) == 7).all())
+
+
+def test_binding_rejects_bad_buffers():
+    """Tensors that the kernels would read from host memory or write out of
+    bounds are rejected by the Python binding before any launch (the C ABI
+    takes raw pointers and cannot see extents or devices)."""
+    M, H = 4, 256
+    x = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros_like(x)
+    w = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    vals = torch.full((M, H), 7, dtype=torch.uint8, device="cuda")
+    sc = torch.full((M, H // 32), 9, dtype=torch.uint8, device="cuda")
+    nrm = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    norm = lambda **k: afq.fused_add_rmsnorm_quant(x if "x" not in k else k.pop("x"),
+                                                   w if "w" not in k else k.pop("w"), 1e-6,
+                                                   mode=afq.MXFP8, **k)
+    bad = [
+        ("host weight", lambda: norm(w=w.cpu())),
+        ("host residual", lambda: norm(residual=r.cpu())),
+        ("short values", lambda: norm(out=(vals[: M - 1], sc, None))),
+        ("strided values", lambda: norm(out=(vals.view(H, M).t(), sc, None))),
+        ("fp32 MX scales", lambda: norm(out=(vals, sc.view(torch.float32)[:, :2].contiguous(), None))),
+        ("short scales", lambda: norm(out=(vals, sc[:, :4].contiguous(), None))),
+        ("fp16 copy of bf16 rows", lambda: norm(out=(vals, sc, nrm.view(torch.float16)))),
+        ("host values", lambda: norm(out=(vals.cpu(), sc, None))),
+        ("short residual_out", lambda: norm(residual=r, residual_out=r[: M - 1])),
+        ("fp16 residual_out", lambda: norm(residual=r, residual_out=r.view(torch.float16))),
+        ("residual_out alone", lambda: norm(residual_out=r)),
+        ("silu short values", lambda: afq.silu_mul_quant(torch.zeros((M, 2 * H), dtype=torch.bfloat16, device="cuda"),
+                                                         afq.MXFP8, out=(vals[:, : H // 2], sc, None))),
+        ("quant with a copy buffer", lambda: afq.fp8_quant(x, afq.MXFP8, out=(vals, sc, nrm))),
+    ]
+    for name, call in bad:
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(name)
+    torch.cuda.synchronize()
+    assert bool((vals == 7).all()) and bool((sc == 9).all())
 
 
 # ------------------------------------------------- rounding-point variants
