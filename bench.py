@@ -399,7 +399,34 @@ PROFILE_WORKLOADS = {
                                          sets=rotation_sets(silu_bytes(4096, 12288, mode="b128"))),
     "silu_b128_i3072": lambda: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128",
                                         sets=rotation_sets(silu_bytes(16384, 3072, mode="b128"))),
+    # decode sizes, hot (one buffer set), launched by graph replay as the
+    # sweep times them
+    "norm_mx_m8": lambda: NormCase(8, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal",
+                                   w_param=0.1, kind="gemma", mode="mx"),
+    "silu_mx_i768_m8": lambda: SiluCase(8, 768, seed=0, std=2.0, mode="mx"),
 }
+PROFILE_BY_GRAPH = {"norm_mx_m8", "silu_mx_i768_m8"}
+
+
+def replay_launches(fn, launches, per_graph=200):
+    """Run about `launches` launches of fn as replays of a captured graph of
+    `per_graph` launches (the decode timing method), for profiler runs."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(per_graph):
+                fn()
+    torch.cuda.current_stream().wait_stream(st)
+    for i in range(max(1, -(-launches // per_graph))):
+        g.replay()
+        if i % 8 == 7:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 # ----------------------------------------------------------------- CPU leg
@@ -467,8 +494,11 @@ def main():
             del head
             torch.cuda.empty_cache()
             work = PROFILE_WORKLOADS[args.profile]()
-        for _ in range(args.warmup + args.steps):
-            work()
+        if args.profile in PROFILE_BY_GRAPH:
+            replay_launches(work, args.warmup + args.steps)
+        else:
+            for _ in range(args.warmup + args.steps):
+                work()
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
         for _ in range(5):
