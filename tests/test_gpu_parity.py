@@ -421,6 +421,47 @@ def test_bitwise_determinism_many_runs():
     torch.cuda.synchronize()
 
 
+GRAPH_ROW_COUNTS = list(range(1, 65)) + list(range(72, 513, 8))
+
+
+@pytest.mark.parametrize("mode,kind", [("mx", "gemma"), ("b128", "standard"), ("pt", "standard")])
+def test_norm_every_graph_row_count(mode, kind):
+    """Every row count 1..64 and every graph-capture size up to 512 (steps of
+    8), at hidden 2048: each launch on the first M rows of one 512-row input
+    matches the oracle's first M rows (rows are independent, so this is also
+    batch invariance), and row 0 is bit-identical across all M."""
+    d = inputs.norm_inputs(512, 2048, seed=21, x_std=3.0, r_std=1.0,
+                           w_kind="normal" if kind == "gemma" else "uniform",
+                           w_param=0.1 if kind == "gemma" else 0.5)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind=kind, mode=mode)
+    first = None
+    for M in GRAPH_ROW_COUNTS:
+        gpu = run_norm(d["x"][:M], d["w"], r=d["r"][:M], kind=kind, mode=mode)
+        sub = {k: ref[k][:M] for k in ("h", "normed", "values", "scales")}
+        check_norm(gpu, sub, mode, "bf16", f"rows{M}-{mode}")
+        row0 = (gpu["values"][0].tobytes(), np.ascontiguousarray(gpu["scales"][0]).tobytes(),
+                gpu["normed"][0].tobytes())
+        first = first or row0
+        assert row0 == first, f"row 0 differs at M={M}"
+
+
+@pytest.mark.parametrize("mode,I", [("mx", 768), ("b128", 2176)])
+def test_silu_every_graph_row_count(mode, I):
+    """SiLU-and-mul at every row count 1..64 and every graph size up to 512,
+    on prefixes of one 512-row input, against the oracle's rows."""
+    gu = inputs.gate_up_inputs(512, I, seed=22, std=2.0)
+    ref = orc.silu_quant(gu, MODE[mode], threads=8)
+    for M in GRAPH_ROW_COUNTS:
+        gpu = _run_silu(gu[:M], mode)
+        if mode == "b128":
+            assert np.array_equal(gpu["values"], ref["values"][:M]), M
+            assert np.array_equal(gpu["scales"].view(np.uint32), ref["scales"][:M].view(np.uint32)), M
+        else:
+            check_codes(gpu["values"], ref["values"][:M], f"silu-mx rows{M}")
+            check_scales(gpu["scales"], ref["scales"][:M], 0, f"silu-mx rows{M}")
+            check_dtype16(gpu["act"], ref["act"][:M], f"silu-mx rows{M} act")
+
+
 def test_graph_replay_equals_eager():
     d = inputs.norm_inputs(32, 6144, seed=13, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
     xt, wt, rt = dev16(d["x"]), dev16(d["w"]), dev16(d["r"])
