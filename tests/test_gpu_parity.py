@@ -32,7 +32,7 @@ def test_norm_gemma_mx_h6144(M):
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
 @pytest.mark.parametrize("kind", ["gemma", "standard"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("H,M", [(4096, 33), (2048, 5), (1024, 130), (512, 9)])
+@pytest.mark.parametrize("H,M", [(6144, 17), (4096, 33), (2048, 5), (1024, 130), (512, 9)])
 def test_norm_modes(mode, kind, dtype, H, M):
     d = inputs.norm_inputs(M, H, seed=3, x_std=1.0, r_std=1.0,
                            w_kind="uniform" if kind == "standard" else "normal",
@@ -75,17 +75,21 @@ def test_norm_inplace_residual():
     check_dtype16(host16(rt), ref["h"], "inplace h", exact=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
-def test_norm_edge_rows(mode):
+def test_norm_edge_rows(mode, dtype):
+    """The edge rows in both dtypes (in fp16 the tiny row underflows to zero
+    and the dominated row's small entries become fp16 subnormals)."""
     H = 2048
     rows = inputs.edge_rows(H)
-    x = inputs.to_bits(rows)
-    r = inputs.to_bits(np.zeros_like(rows))
-    w = inputs.to_bits(np.random.default_rng(3).uniform(0.5, 1.5, H))
+    x = inputs.to_bits(rows, dtype)
+    r = inputs.to_bits(np.zeros_like(rows), dtype)
+    w = inputs.to_bits(np.random.default_rng(3).uniform(0.5, 1.5, H), dtype)
     for kind in ("standard", "gemma"):
-        gpu = run_norm(x, w, r=r, kind=kind, mode=mode)
-        ref = ref_norm(x, w, r=r, kind=kind, mode=mode)
-        _report(f"edge {mode} {kind}", check_norm(gpu, ref, mode, "bf16", f"edge-{mode}-{kind}"))
+        gpu = run_norm(x, w, r=r, kind=kind, mode=mode, dtype=dtype)
+        ref = ref_norm(x, w, r=r, kind=kind, mode=mode, dtype=dtype)
+        _report(f"edge {mode} {kind} {dtype}",
+                check_norm(gpu, ref, mode, dtype, f"edge-{mode}-{kind}-{dtype}"))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
