@@ -137,14 +137,15 @@ class QuantizedActivation:
     """Codes and scales of a quantised activation (the tuple a quantised
     linear consumes), with the optional rounded activation and residual.
 
-    values   float8_e4m3fn [M, cols]
+    values   float8_e4m3fn [M, cols] (None for a copy-only launch)
     scales   MXFP8: uint8 E8M0 bytes [M, cols/32]; BLOCK128: float32
-             [M, cols/128]; PER_TOKEN: float32 [M, 1]
+             [M, cols/128]; PER_TOKEN: float32 [M, 1] (None for a copy-only
+             launch)
     normed   the rounded activation in its dtype, or None
     residual the updated residual h = x + r (norm with residual), or None
     """
-    values: torch.Tensor
-    scales: torch.Tensor
+    values: Optional[torch.Tensor]
+    scales: Optional[torch.Tensor]
     normed: Optional[torch.Tensor]
     residual: Optional[torch.Tensor]
     mode: int
@@ -222,17 +223,24 @@ def _check_buf(t: torch.Tensor, numel: int, dtypes, device: torch.device, name: 
 _CODE_DTYPES = (torch.float8_e4m3fn, torch.uint8)
 
 
-def _alloc_out(mode, M, cols, device, normed_dtype, want, out):
+def _alloc_out(mode, M, cols, device, normed_dtype, want, out, quantize=True):
     sshape, sdtype = _scales_shape(mode, M, cols)
     if out is not None:
         if len(out) != 3:
             raise ValueError("out must be a (values, scales, normed) tuple")
         values, scales, normed = out
+        if not quantize:
+            if values is not None or scales is not None or normed is None:
+                raise ValueError("a copy-only launch takes out = (None, None, copy)")
+            _check_buf(normed, M * cols, (normed_dtype,), device, "out normed")
+            return None, None, normed
         _check_buf(values, M * cols, _CODE_DTYPES, device, "out values")
         _check_buf(scales, sshape[0] * sshape[1], (sdtype,), device, "out scales")
         if normed is not None:
             _check_buf(normed, M * cols, (normed_dtype,), device, "out normed")
         return values, scales, normed
+    if not quantize:
+        return None, None, torch.empty((M, cols), dtype=normed_dtype, device=device)
     values = torch.empty((M, cols), dtype=torch.float8_e4m3fn, device=device)
     scales = torch.empty(sshape, dtype=sdtype, device=device)
     normed = torch.empty((M, cols), dtype=normed_dtype, device=device) if want else None
@@ -262,6 +270,7 @@ def fused_add_rmsnorm_quant(
     inplace: bool = False,
     want_normed: bool = False,
     quant_input: int = QIN_DEFAULT,
+    quantize: bool = True,
     out=None,
     stream=None,
 ):
@@ -276,6 +285,8 @@ def fused_add_rmsnorm_quant(
     want_normed  also return the normed rows rounded to the input dtype.
     quant_input  QIN_DEFAULT: quantise the dtype-rounded normed rows;
                  QIN_FP32 (1x128 / per-token): quantise the fp32 normed value.
+    quantize     False: the norm of the unfused chain -- only the normed rows
+                 (and the residual) are written; values and scales are None.
     out          optional preallocated (values, scales, normed) per segment
                  (a tuple, or a list of tuples for two segments).
     Returns a QuantizedActivation, or a list of two for two segments.
@@ -309,7 +320,8 @@ def fused_add_rmsnorm_quant(
         if wi.dim() != 1 or wi.shape[0] != xi.shape[1] or not wi.is_contiguous():
             raise ValueError("weight must be a contiguous [cols] tensor")
         cols = xi.shape[1]
-        values, scales, normed = _alloc_out(mode, M, cols, device, dtype, want_normed, outs[i])
+        values, scales, normed = _alloc_out(mode, M, cols, device, dtype, want_normed, outs[i],
+                                            quantize)
         seg = d.seg[i]
         seg.x, seg.x_row_stride, seg.weight, seg.cols = xi.data_ptr(), xi.stride(0), wi.data_ptr(), cols
         seg.out.values, seg.out.scales, seg.out.normed = _ptr(values), _ptr(scales), _ptr(normed)
@@ -336,13 +348,16 @@ def fused_add_rmsnorm_quant(
 
 
 def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
-                   quant_input: int = QIN_DEFAULT, out=None, stream=None) -> QuantizedActivation:
+                   quant_input: int = QIN_DEFAULT, quantize: bool = True, out=None,
+                   stream=None) -> QuantizedActivation:
     """SiLU-and-mul of a bf16 [M, 2I] row ([gate | up]) + FP8 quantisation.
 
     MXFP8 quantises the fp32 activation; BLOCK128 rounds silu and the product
     to bf16 first (the unfused SiluAndMul).  With MXFP8, quant_input=QIN_BF16
     quantises the bf16-rounded activation instead (the unfused chain's
-    rounding).  want_act also returns the bf16 activation.
+    rounding).  want_act also returns the bf16 activation.  quantize=False:
+    the SiLU-and-mul of the unfused chain -- only the bf16 activation (rounded
+    as `mode` rounds it) is written; values and scales are None.
     """
     lib = load()
     mode = _mode(mode)
@@ -353,7 +368,8 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
     if two_i % 2:
         raise ValueError("gate_up must have an even number of columns")
     I = two_i // 2
-    values, scales, act = _alloc_out(mode, M, I, gate_up.device, torch.bfloat16, want_act, out)
+    values, scales, act = _alloc_out(mode, M, I, gate_up.device, torch.bfloat16, want_act, out,
+                                     quantize)
     d = _ActDesc()
     d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
     d.quant_input = int(quant_input)

@@ -69,10 +69,11 @@ int64_t scale_elt(int mode) { return mode == AFQ_MXFP8 ? 1 : 4; }
 
 bool valid_mode(int m) { return m == AFQ_MXFP8 || m == AFQ_BLOCK128 || m == AFQ_PER_TOKEN; }
 
-// Row width rules shared by every entry point.
-bool width_ok(int64_t cols, int mode)
+// Row width rules shared by every entry point (a copy-only launch has no
+// quantisation groups: its widths need only be whole 16-byte chunks).
+bool width_ok(int64_t cols, int mode, bool quant = true)
 {
-    return cols > 0 && cols <= AFQ_MAX_COLS && cols % 8 == 0 && cols % group_of(mode) == 0;
+    return cols > 0 && cols <= AFQ_MAX_COLS && cols % 8 == 0 && (!quant || cols % group_of(mode) == 0);
 }
 
 // Outputs must not overlap each other or any input.
@@ -132,13 +133,18 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
     if (!(std::isfinite(d->eps) && d->eps >= 0.0f)) return AFQ_ERR_ARG;
     if (d->quant_input == AFQ_QIN_BF16) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_FP32 && d->mode == AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
-    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
     if (d->nseg != 1 && d->nseg != 2) return AFQ_ERR_SHAPE;
+    // copy only (the norm of the unfused chain): no codes or scales anywhere
+    bool quant = false;
+    for (int s = 0; s < d->nseg; ++s)
+        quant = quant || d->seg[s].out.values || d->seg[s].out.scales;
+    if (!quant && d->quant_input != AFQ_QIN_DEFAULT) return AFQ_ERR_UNSUPPORTED;
+    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
     const bool has_res = d->residual_in != nullptr || d->residual_out != nullptr;
     if (has_res && d->nseg != 1) return AFQ_ERR_SHAPE;
     for (int s = 0; s < d->nseg; ++s) {
         const afq_norm_seg &g = d->seg[s];
-        if (!width_ok(g.cols, d->mode)) return AFQ_ERR_SHAPE;
+        if (!width_ok(g.cols, d->mode, quant)) return AFQ_ERR_SHAPE;
         if (!stride_ok(g.x_row_stride, g.cols)) return AFQ_ERR_SHAPE;
     }
     if (d->nseg == 2 && (d->seg[0].cols + d->seg[1].cols) > AFQ_MAX_COLS) return AFQ_ERR_SHAPE;
@@ -147,15 +153,16 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
     if (has_res && (!d->residual_in || !d->residual_out)) return AFQ_ERR_NULL;
     for (int s = 0; s < d->nseg; ++s) {
         const afq_norm_seg &g = d->seg[s];
-        if (!g.x || !g.weight || !g.out.values || !g.out.scales) return AFQ_ERR_NULL;
+        if (!g.x || !g.weight) return AFQ_ERR_NULL;
+        if (quant ? (!g.out.values || !g.out.scales) : !g.out.normed) return AFQ_ERR_NULL;
     }
 
     const int64_t elt = 2;
     for (int s = 0; s < d->nseg; ++s) {
         const afq_norm_seg &g = d->seg[s];
         if (!aligned(g.x, 16) || (g.x_row_stride * elt) % 16 != 0) return AFQ_ERR_ALIGN;
-        if (!aligned(g.weight, 16) || !aligned(g.out.values, 16) || !aligned(g.out.scales, 4))
-            return AFQ_ERR_ALIGN;
+        if (!aligned(g.weight, 16)) return AFQ_ERR_ALIGN;
+        if (quant && (!aligned(g.out.values, 16) || !aligned(g.out.scales, 4))) return AFQ_ERR_ALIGN;
         if (g.out.normed && !aligned(g.out.normed, 16)) return AFQ_ERR_ALIGN;
     }
     if (has_res && (!aligned(d->residual_in, 16) || !aligned(d->residual_out, 16)))
@@ -212,6 +219,7 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
     p.dtype = d->dtype;
     p.mode = d->mode;
     p.qin = d->quant_input;
+    p.quant = quant ? 1 : 0;
     return launched(afq::launch_norm(p, stream));
 }
 
@@ -223,13 +231,17 @@ int silu_mul_quant(const afq_act_desc *d, void *stream)
     if (d->mode == AFQ_PER_TOKEN) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_FP32) return AFQ_ERR_UNSUPPORTED;
     if (d->quant_input == AFQ_QIN_BF16 && d->mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
+    // copy only (the SiLU-and-mul of the unfused chain): no codes or scales
+    const bool quant = d->out.values || d->out.scales;
+    if (!quant && d->quant_input != AFQ_QIN_DEFAULT) return AFQ_ERR_UNSUPPORTED;
     if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
-    if (!width_ok(d->I, d->mode)) return AFQ_ERR_SHAPE;
+    if (!width_ok(d->I, d->mode, quant)) return AFQ_ERR_SHAPE;
     if (!stride_ok(d->gate_up_row_stride, 2 * d->I)) return AFQ_ERR_SHAPE;
     if (d->M == 0) return AFQ_OK;
-    if (!d->gate_up || !d->out.values || !d->out.scales) return AFQ_ERR_NULL;
+    if (!d->gate_up) return AFQ_ERR_NULL;
+    if (quant ? (!d->out.values || !d->out.scales) : !d->out.normed) return AFQ_ERR_NULL;
     if (!aligned(d->gate_up, 16) || (d->gate_up_row_stride * 2) % 16 != 0) return AFQ_ERR_ALIGN;
-    if (!aligned(d->out.values, 16) || !aligned(d->out.scales, 4)) return AFQ_ERR_ALIGN;
+    if (quant && (!aligned(d->out.values, 16) || !aligned(d->out.scales, 4))) return AFQ_ERR_ALIGN;
     if (d->out.normed && !aligned(d->out.normed, 16)) return AFQ_ERR_ALIGN;
 
     const int64_t M = d->M, I = d->I;
@@ -253,6 +265,7 @@ int silu_mul_quant(const afq_act_desc *d, void *stream)
     p.I = (int32_t)I;
     p.mode = d->mode;
     p.qin = d->quant_input;
+    p.quant = quant ? 1 : 0;
     return launched(afq::launch_act(p, stream));
 }
 

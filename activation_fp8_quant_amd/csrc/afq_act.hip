@@ -142,8 +142,10 @@ __device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8],
 
 // QBF16 (MXFP8 only): the bf16-first variant, which quantises the fp32
 // activation rounded to bf16 (the value the unfused chain stores and then
-// quantises) instead of the fp32 activation itself.
-template <int MODE, int CPL, bool QBF16>
+// quantises) instead of the fp32 activation itself.  QUANT false: the
+// SiLU-and-mul of the unfused chain, which writes only the bf16 activation
+// (rounded as MODE's activation is) and no codes or scales.
+template <int MODE, int CPL, bool QBF16, bool QUANT>
 __global__ void __launch_bounds__(256)
 act_quant_kernel(const ActArgs a)
 {
@@ -171,7 +173,16 @@ act_quant_kernel(const ActArgs a)
         float g[8], v[8];
         unpack8<kBF16>(gv[k], g);
         unpack8<kBF16>(uv[k], v);
-        if constexpr (MODE == kMX) {
+        if constexpr (!QUANT) {
+            // the unfused SiLU-and-mul: the activation alone
+            const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
+            float sg[8];
+            if constexpr (MODE == kMX) silu_f32x8(g, sg);
+            else silu_bf16x8(g, gv[k], sg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+            stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
+        } else if constexpr (MODE == kMX) {
             const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
             uint2 q;
             float sg[8];
@@ -193,11 +204,11 @@ act_quant_kernel(const ActArgs a)
 }
 
 // ================================================================ launcher
-template <int MODE, int CPL, bool QBF16>
+template <int MODE, int CPL, bool QBF16, bool QUANT = true>
 static hipError_t go_act(const ActArgs &a, hipStream_t st)
 {
     const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
-    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL, QBF16>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL, QBF16, QUANT>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -211,16 +222,18 @@ int launch_act(const ActPlan &p, void *stream)
         ActArgs a;
         a.gu = p.gu + r0 * p.gu_pitch;
         a.gu_pitch = p.gu_pitch;
-        a.values = p.values + r0 * p.I;
-        a.scales = p.scales + r0 * scale_row_bytes(p.mode, p.I);
-        a.act = p.act ? p.act + r0 * p.I * 2 : nullptr;
+        a.values = offset_or_null(p.values, r0 * p.I);
+        a.scales = offset_or_null(p.scales, r0 * scale_row_bytes(p.mode, p.I));
+        a.act = offset_or_null(p.act, r0 * p.I * 2);
         a.C = C;
         a.I = p.I;
         a.total = (uint32_t)(rows * C);
         a.dc = divc((uint32_t)C);
-        hipError_t e = p.mode != kMX ? go_act<kB128, 1, false>(a, st)
-                     : p.qin == 2   ? go_act<kMX, 1, true>(a, st)
-                                    : go_act<kMX, 1, false>(a, st);
+        hipError_t e = !p.quant      ? (p.mode == kMX ? go_act<kMX, 1, false, false>(a, st)
+                                                     : go_act<kB128, 1, false, false>(a, st))
+                     : p.mode != kMX ? go_act<kB128, 1, false>(a, st)
+                     : p.qin == 2    ? go_act<kMX, 1, true>(a, st)
+                                     : go_act<kMX, 1, false>(a, st);
         if (e != hipSuccess) return (int)e;
     }
     return 0;

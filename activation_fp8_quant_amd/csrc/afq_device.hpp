@@ -23,6 +23,7 @@ namespace afq {
 // dtype / mode tags (match afq.h)
 constexpr int kBF16 = 0, kFP16 = 1, kFP32 = 2;
 constexpr int kMX = 0, kB128 = 1, kPT = 2;
+constexpr int kNone = 3; // copy only: the launch writes no codes or scales
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -28,6 +28,7 @@ struct NormPlan {
     int32_t dtype;          // 0 bf16, 1 fp16
     int32_t mode;           // 0 MX, 1 B128, 2 PT
     int32_t qin;            // 0 dtype-rounded row, 1 fp32 normed value (B128 / PT)
+    int32_t quant;          // 1 quantise; 0 copy only (values, scales nullptr)
 };
 
 struct ActPlan {
@@ -38,8 +39,9 @@ struct ActPlan {
     uint8_t *act;           // optional bf16 [M, I]
     int64_t M;
     int32_t I;
-    int32_t mode;
+    int32_t mode;           // also the activation's rounding when copy only
     int32_t qin;            // 0 mode default, 2 bf16-rounded activation (MX)
+    int32_t quant;          // 1 quantise; 0 copy only (values, scales nullptr)
 };
 
 struct QuantPlan {

@@ -74,7 +74,11 @@ static inline int64_t row_rows_per_launch(int NT, int R)
 // Bytes of scales per row of `cols` elements in quant mode `mode`.
 static inline int64_t scale_row_bytes(int mode, int32_t cols)
 {
-    return mode == kMX ? cols / 32 : mode == kB128 ? 4 * (cols / 128) : 4;
+    return mode == kMX ? cols / 32 : mode == kB128 ? 4 * (cols / 128) : mode == kPT ? 4 : 0;
 }
+
+// p + off for a buffer that may be absent (nullptr stays nullptr).
+template <typename T>
+static inline T *offset_or_null(T *p, int64_t off) { return p ? p + off : nullptr; }
 
 } // namespace afq

@@ -225,8 +225,10 @@ norm_quant_kernel(const NormArgs a)
         }
     }
 
-    // ---- quantise
-    if constexpr (MODE == kPT) {
+    // ---- quantise (nothing more for a copy-only launch)
+    if constexpr (MODE == kNone) {
+        return;
+    } else if constexpr (MODE == kPT) {
         if (has0) am0 = max_wave(am0);
         if constexpr (NSEG > 1)
             if (has1) am1 = max_wave(am1);
@@ -309,6 +311,7 @@ static hipError_t go_norm_mode(const NormArgs &a, int mode, bool f32q, bool gemm
                                hipStream_t st)
 {
     switch (mode) {
+    case kNone: return go_norm_kind<DT, kNone, false>(a, gemma, nseg, CPL, st);
     case kMX: return go_norm_kind<DT, kMX, false>(a, gemma, nseg, CPL, st);
     case kB128:
         return f32q ? go_norm_kind<DT, kB128, true>(a, gemma, nseg, CPL, st)
@@ -330,7 +333,8 @@ int launch_norm(const NormPlan &p, void *stream)
     a.eps = p.eps;
     a.C0 = p.seg[0].chunks;
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
-    const RowShapeRt sh = row_shape(a.C, p.M, p.mode == kPT);
+    const int mode = p.quant ? p.mode : kNone;
+    const RowShapeRt sh = row_shape(a.C, p.M, mode == kPT);
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;
@@ -348,14 +352,14 @@ int launch_norm(const NormPlan &p, void *stream)
         for (int s = 0; s < 2; ++s) {
             const NormSegPlan &g = a.seg[s];
             b.seg[s].x = g.x + r0 * g.x_pitch;
-            b.seg[s].values = g.values + r0 * g.cols;
-            b.seg[s].scales = g.scales + r0 * scale_row_bytes(p.mode, g.cols);
-            b.seg[s].normed = g.normed ? g.normed + r0 * g.cols * 2 : nullptr;
+            b.seg[s].values = offset_or_null(g.values, r0 * g.cols);
+            b.seg[s].scales = offset_or_null(g.scales, r0 * scale_row_bytes(mode, g.cols));
+            b.seg[s].normed = offset_or_null(g.normed, r0 * g.cols * 2);
         }
         b.res_in = a.res_in ? a.res_in + r0 * a.C0 * 16 : nullptr;
         b.res_out = a.res_out ? a.res_out + r0 * a.C0 * 16 : nullptr;
-        const hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(b, p.mode, f32q, gemma, p.nseg, sh.CPL, st)
-                                              : go_norm_mode<kBF16>(b, p.mode, f32q, gemma, p.nseg, sh.CPL, st);
+        const hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st)
+                                              : go_norm_mode<kBF16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st);
         if (e != hipSuccess) return (int)e;
     }
     return 0;

@@ -52,6 +52,12 @@ HBM_PEAK_GBS = 8000.0
 # pages' per-launch figures (MI355X, their Triton kernels; context, not targets)
 PAGE_NORM_US = {8: 2.71, 16: 2.77, 32: 2.80, 64: 2.96, 128: 3.29, 192: 3.65}
 PAGE_SWIGLU_US = {8: 1.83, 16: 1.93, 32: 1.95, 64: 1.94, 128: 1.90, 192: 1.95}
+# the same table's unfused columns: norm + separate quant (2 launches) and
+# the time the fusion saves; swiglu + separate quant and its saving
+PAGE_NORM_CHAIN_US = {8: 4.27, 16: 4.32, 32: 4.40, 64: 4.79, 128: 5.55, 192: 6.94}
+PAGE_NORM_SAVED_US = {8: 1.56, 16: 1.55, 32: 1.60, 64: 1.83, 128: 2.26, 192: 3.29}
+PAGE_SWIGLU_CHAIN_US = {8: 3.82, 16: 3.96, 32: 3.97, 64: 4.00, 128: 4.06, 192: 4.04}
+PAGE_SWIGLU_SAVED_US = {8: 1.99, 16: 2.03, 32: 2.02, 64: 2.06, 128: 2.16, 192: 2.09}
 
 
 # ----------------------------------------------------------- byte formulas
@@ -234,6 +240,70 @@ class TwoSegCase:
                                          kind=self.afq.STANDARD, out=outs)
 
 
+class NormChainCase:
+    """The unfused chain on this library's kernels: a copy-only add + RMSNorm
+    launch (residual and normed rows), then the standalone quantiser on its
+    rows -- two launches per call."""
+
+    def __init__(self, M, H, *, seed, x_std, r_std, w_kind, w_param, kind, mode, sets=1):
+        import torch
+        import activation_fp8_quant_amd as afq
+        from activation_fp8_quant_amd import inputs
+        self.afq = afq
+        self.mode = {"mx": afq.MXFP8, "b128": afq.BLOCK128, "pt": afq.PER_TOKEN}[mode]
+        self.kind = {"gemma": afq.GEMMA, "standard": afq.STANDARD}[kind]
+        d = inputs.norm_inputs(M, H, seed=seed, x_std=x_std, r_std=r_std, w_kind=w_kind,
+                               w_param=w_param)
+        x, self.w, r = _dev16(d["x"]), _dev16(d["w"]), _dev16(d["r"])
+        self.sets = []
+        for i in range(sets):
+            xi, ri = (x, r) if i == 0 else (x.clone(), r.clone())
+            plain = afq.fused_add_rmsnorm_quant(xi, self.w, 1e-6, mode=self.mode, kind=self.kind,
+                                                residual=ri, quantize=False)
+            q = afq.fp8_quant(plain.normed, self.mode)
+            self.sets.append(dict(x=xi, r=ri, rout=plain.residual, normed=plain.normed,
+                                  out=(q.values, q.scales, None)))
+        self.i = 0
+        self.bytes = M * (8 * H + 2 * H + H + H // 32) + 2 * H
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        s = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        self.afq.fused_add_rmsnorm_quant(s["x"], self.w, 1e-6, mode=self.mode, kind=self.kind,
+                                         residual=s["r"], residual_out=s["rout"], quantize=False,
+                                         out=(None, None, s["normed"]))
+        self.afq.fp8_quant(s["normed"], self.mode, out=s["out"])
+
+
+class SiluChainCase:
+    """The unfused SiLU chain on this library's kernels: a copy-only
+    SiLU-and-mul launch (bf16 activation), then the standalone quantiser."""
+
+    def __init__(self, M, I, *, seed, std, mode, sets=1):
+        import torch
+        import activation_fp8_quant_amd as afq
+        from activation_fp8_quant_amd import inputs
+        self.afq = afq
+        self.mode = {"mx": afq.MXFP8, "b128": afq.BLOCK128}[mode]
+        gu = _dev16(inputs.gate_up_inputs(M, I, seed=seed, std=std))
+        self.sets = []
+        for i in range(sets):
+            gi = gu if i == 0 else gu.clone()
+            plain = self.afq.silu_mul_quant(gi, self.mode, quantize=False)
+            q = afq.fp8_quant(plain.normed, self.mode)
+            self.sets.append((gi, plain.normed, (q.values, q.scales, None)))
+        self.i = 0
+        self.bytes = M * (4 * I + 2 * I + 2 * I + I + I // 32)
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        g, act, out = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        self.afq.silu_mul_quant(g, self.mode, quantize=False, out=(None, None, act))
+        self.afq.fp8_quant(act, self.mode, out=out)
+
+
 class QuantCase:
     """The standalone quantiser on a bf16 [M, H] activation (the separate
     quant kernel of an unfused chain)."""
@@ -317,6 +387,7 @@ def run_sweep():
         log(f"{cfg} {name} M={M} {r['cache']}: {us:.2f} us")
         del case
         torch.cuda.empty_cache()
+        return r
 
     # trivial-kernel floor: a one-element fill, timed the same way
     t = torch.zeros(1, device="cuda")
@@ -333,15 +404,29 @@ def run_sweep():
 
     for M in DECODE_M:
         ws = norm_bytes(M, 6144)
-        rec("C1", c1, norm_c1(M), M, ws, hot=True, page_us=PAGE_NORM_US[M], eager=True)
+        fused = rec("C1", c1, norm_c1(M), M, ws, hot=True, page_us=PAGE_NORM_US[M], eager=True)
         if ws >= (1 << 20):
             rec("C1", c1, norm_c1(M), M, ws)
-        rec("C2", "SiLU-and-mul + MXFP8, I=768",
-            lambda k, M=M: SiluCase(M, 768, seed=0, std=2.0, mode="mx", sets=k), M,
-            silu_bytes(M, 768), hot=True, page_us_swiglu_oai=PAGE_SWIGLU_US[M], eager=True)
+        fused_s = rec("C2", "SiLU-and-mul + MXFP8, I=768",
+                      lambda k, M=M: SiluCase(M, 768, seed=0, std=2.0, mode="mx", sets=k), M,
+                      silu_bytes(M, 768), hot=True, page_us_swiglu_oai=PAGE_SWIGLU_US[M], eager=True)
         rec("f1", "standalone MXFP8 quant of a bf16 [M, 6144] (the separate quant)",
             lambda k, M=M: QuantCase(M, 6144, seed=0, std=3.0, mode="mx", sets=k), M,
             M * (3 * 6144 + 6144 // 32), hot=True)
+        # the unfused chains on this library's kernels, and what the fusion saves
+        ch = rec("f1", "unfused chain: copy-only add + Gemma RMSNorm, then MXFP8 quant "
+                 "(2 launches), H=6144",
+                 lambda k, M=M: NormChainCase(M, 6144, seed=0, x_std=3.0, r_std=1.0,
+                                              w_kind="normal", w_param=0.1, kind="gemma",
+                                              mode="mx", sets=k),
+                 M, M * (11 * 6144 + 6144 // 32), hot=True, page_us=PAGE_NORM_CHAIN_US[M])
+        ch["saved_us"] = round(ch["us_per_launch"] - fused["us_per_launch"], 2)
+        ch["page_saved_us"] = PAGE_NORM_SAVED_US[M]
+        ch = rec("f1", "unfused chain: copy-only SiLU-and-mul, then MXFP8 quant (2 launches), "
+                 "I=768", lambda k, M=M: SiluChainCase(M, 768, seed=0, std=2.0, mode="mx", sets=k),
+                 M, M * (9 * 768 + 768 // 32), hot=True, page_us_swiglu_oai=PAGE_SWIGLU_CHAIN_US[M])
+        ch["saved_us"] = round(ch["us_per_launch"] - fused_s["us_per_launch"], 2)
+        ch["page_saved_us_swiglu_oai"] = PAGE_SWIGLU_SAVED_US[M]
     for M in (256, 1024):
         rec("C1", c1, norm_c1(M), M, norm_bytes(M, 6144))
     for M in (1, 32, 256, 4096):

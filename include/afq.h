@@ -81,6 +81,21 @@
  *   - Overlap between buffers is judged on each buffer's byte span from its
  *     first to its last byte.
  *   - Inputs are assumed finite; NaN or Inf inputs give unspecified codes.
+ *
+ * Copy-only launches (ABI 3): when out.values and out.scales are both NULL
+ * (in every segment of a norm launch), fused_add_rmsnorm_quant and
+ * silu_mul_quant quantise nothing and write only the rounded activation
+ * out.normed, which is then required (and, for the norm, the updated
+ * residual).  These are the first kernels of the unfused chains: norm ->
+ * fp8_quant and SiLU-and-mul -> fp8_quant, which the fused launches replace
+ * (vLLM pull request 65478, "Kernel-level measurements": the "norm +
+ * separate quant" and "swiglu + separate quant" columns).  The copy is the
+ * same as a quantising launch's copy: u for the norm (any mode), and for
+ * SiLU-and-mul the activation rounded to bf16 as `mode` rounds it (MXFP8:
+ * bf16(a) of the fp32 activation; BLOCK128: bf16(bf16(silu) * up)).  Widths
+ * need only be multiples of 8; quant_input must be AFQ_QIN_DEFAULT
+ * (otherwise AFQ_ERR_UNSUPPORTED).  Only one of values / scales being NULL
+ * is AFQ_ERR_NULL.
  */
 #ifndef AFQ_H
 #define AFQ_H
@@ -91,7 +106,7 @@
 extern "C" {
 #endif
 
-#define AFQ_ABI_VERSION 2
+#define AFQ_ABI_VERSION 3
 
 /* Return codes. */
 enum {
@@ -143,13 +158,15 @@ enum { AFQ_QIN_DEFAULT = 0, AFQ_QIN_FP32 = 1, AFQ_QIN_BF16 = 2 };
 /*
  * A quantised activation (the tuple a quantised linear consumes: codes,
  * scales, and optionally the activation rounded to its dtype).
- *   values  e4m3fn codes, [rows, cols] dense row-major.  Required.
+ *   values  e4m3fn codes, [rows, cols] dense row-major.  Required, unless
+ *           values and scales are both NULL (a copy-only launch).
  *   scales  MXFP8: uint8 E8M0 [rows, cols/32]; BLOCK128: float
  *           [rows, cols/128]; PER_TOKEN: float [rows, 1].  Dense
- *           row-major, unswizzled.  Required; 4-byte aligned.
- *   normed  optional [rows, cols] dense copy of the rounded activation in
- *           the activation dtype (the norm output u, or for SiLU-and-mul the
- *           bf16 activation); NULL = not written.
+ *           row-major, unswizzled.  Required as values is; 4-byte aligned.
+ *   normed  [rows, cols] dense copy of the rounded activation in the
+ *           activation dtype (the norm output u, or for SiLU-and-mul the
+ *           bf16 activation); NULL = not written.  Required by a copy-only
+ *           launch.
  */
 typedef struct afq_qact {
     void *values;

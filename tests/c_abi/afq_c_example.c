@@ -5,8 +5,9 @@
  * include/afq.h on seeded inputs, copies the outputs back and checks them
  * against the CPU oracle (oracle/afq_oracle.c, linked into this test
  * program): the fused add + Gemma RMSNorm + MXFP8 + copy, the 1x128
- * SiLU-and-mul and the standalone per-token quantiser.  Also checks the
- * version and an error path.  Prints one line per check; exits non-zero on
+ * SiLU-and-mul and the standalone per-token quantiser; and that the unfused
+ * chain (a copy-only norm launch, then fp8_quant) reproduces the fused
+ * launch bit for bit.  Also checks the version and an error path.  Prints one line per check; exits non-zero on
  * the first failure.
  */
 #include "afq.h"
@@ -129,6 +130,30 @@ int main(void)
         compare16("norm bf16 copy", gn, on, M * H, 0);
         compare_codes("norm MXFP8 codes", gq, oq, M * H);
         compare_bytes("norm E8M0 scales", gs, os, M * H / 32, 1);
+
+        /* the unfused chain: a copy-only norm launch (values and scales NULL),
+         * then fp8_quant of its rows -- bit-identical to the fused launch */
+        void *dh2 = dmalloc(2 * M * H), *dn2 = dmalloc(2 * M * H), *dq2 = dmalloc(M * H), *ds2 = dmalloc(M * H / 32);
+        d.residual_out = dh2;
+        d.seg[0].out.values = NULL; d.seg[0].out.scales = NULL; d.seg[0].out.normed = dn2;
+        stt = fused_add_rmsnorm_quant(&d, st);
+        if (stt != AFQ_OK) FAIL("copy-only fused_add_rmsnorm_quant: %s", afq_status_string(stt));
+        afq_quant_desc qd;
+        memset(&qd, 0, sizeof qd);
+        qd.M = M; qd.cols = H; qd.x = dn2; qd.x_row_stride = H; qd.dtype = AFQ_BF16; qd.mode = AFQ_MXFP8;
+        qd.out.values = dq2; qd.out.scales = ds2;
+        stt = fp8_quant(&qd, st);
+        if (stt != AFQ_OK) FAIL("fp8_quant of the copy-only rows: %s", afq_status_string(stt));
+        CHECK_HIP(hipStreamSynchronize(st));
+        uint16_t *ch = malloc(2 * M * H), *cn = malloc(2 * M * H);
+        uint8_t *cq = malloc(M * H), *cs = malloc(M * H / 32);
+        down(ch, dh2, 2 * M * H); down(cn, dn2, 2 * M * H); down(cq, dq2, M * H); down(cs, ds2, M * H / 32);
+        if (memcmp(ch, gh, 2 * M * H) || memcmp(cn, gn, 2 * M * H) || memcmp(cq, gq, M * H) || memcmp(cs, gs, M * H / 32))
+            FAIL("unfused chain (copy-only norm -> fp8_quant) differs from the fused launch");
+        printf("unfused chain (copy-only norm -> fp8_quant): bit-identical to the fused launch\n");
+        CHECK_HIP(hipFree(dh2)); CHECK_HIP(hipFree(dn2)); CHECK_HIP(hipFree(dq2)); CHECK_HIP(hipFree(ds2));
+        free(ch); free(cn); free(cq); free(cs);
+
         CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dr)); CHECK_HIP(hipFree(dw)); CHECK_HIP(hipFree(dh));
         CHECK_HIP(hipFree(dq)); CHECK_HIP(hipFree(ds)); CHECK_HIP(hipFree(dn));
         free(x); free(r); free(w); free(gh); free(gn); free(oh); free(on); free(gq); free(gs); free(oq); free(os);

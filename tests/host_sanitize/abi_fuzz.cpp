@@ -37,16 +37,21 @@ int launch_norm(const NormPlan &p, void *)
     require(p.mode >= 0 && p.mode <= 2 && (p.kind == 0 || p.kind == 1) && (p.dtype == 0 || p.dtype == 1),
             "norm: enums");
     require(p.qin == 0 || (p.qin == 1 && p.mode != AFQ_MXFP8), "norm: quant_input");
+    require(p.quant == 1 || (p.quant == 0 && p.qin == 0), "norm: copy only reads the default input");
     require((p.res_in == nullptr) == (p.res_out == nullptr), "norm: residual pair");
     require(p.res_in == nullptr || p.nseg == 1, "norm: residual with one segment");
     require(p.res_in == nullptr || (al(p.res_in, 16) && al(p.res_out, 16)), "norm: residual alignment");
     int64_t total = 0;
     for (int s = 0; s < p.nseg; ++s) {
         const NormSegPlan &g = p.seg[s];
-        require(g.cols > 0 && g.cols <= AFQ_MAX_COLS && g.cols % 8 == 0 && g.cols % group(p.mode) == 0,
-                "norm: width");
+        require(g.cols > 0 && g.cols <= AFQ_MAX_COLS && g.cols % 8 == 0 &&
+                    (!p.quant || g.cols % group(p.mode) == 0), "norm: width");
         require(g.chunks == g.cols / 8, "norm: chunks");
-        require(al(g.x, 16) && al(g.w, 16) && al(g.values, 16) && al(g.scales, 4), "norm: pointers");
+        require(al(g.x, 16) && al(g.w, 16), "norm: input pointers");
+        if (p.quant)
+            require(al(g.values, 16) && al(g.scales, 4), "norm: output pointers");
+        else
+            require(!g.values && !g.scales && al(g.normed, 16), "norm: copy-only pointers");
         require(g.normed == nullptr || al(g.normed, 16), "norm: copy pointer");
         require(g.x_pitch >= (int64_t)g.cols * 2 && g.x_pitch % 16 == 0 &&
                     g.x_pitch <= AFQ_MAX_ROW_STRIDE * 2, "norm: pitch");
@@ -61,8 +66,14 @@ int launch_act(const ActPlan &p, void *)
     require(p.M > 0 && p.M <= AFQ_MAX_ROWS, "act: M");
     require(p.mode == AFQ_MXFP8 || p.mode == AFQ_BLOCK128, "act: mode");
     require(p.qin == 0 || (p.qin == 2 && p.mode == AFQ_MXFP8), "act: quant_input");
-    require(p.I > 0 && p.I <= AFQ_MAX_COLS && p.I % 8 == 0 && p.I % group(p.mode) == 0, "act: width");
-    require(al(p.gu, 16) && al(p.values, 16) && al(p.scales, 4), "act: pointers");
+    require(p.quant == 1 || (p.quant == 0 && p.qin == 0), "act: copy only reads the default input");
+    require(p.I > 0 && p.I <= AFQ_MAX_COLS && p.I % 8 == 0 && (!p.quant || p.I % group(p.mode) == 0),
+            "act: width");
+    require(al(p.gu, 16), "act: input pointer");
+    if (p.quant)
+        require(al(p.values, 16) && al(p.scales, 4), "act: output pointers");
+    else
+        require(!p.values && !p.scales && al(p.act, 16), "act: copy-only pointers");
     require(p.act == nullptr || al(p.act, 16), "act: copy pointer");
     require(p.gu_pitch >= (int64_t)p.I * 4 && p.gu_pitch % 16 == 0, "act: pitch");
     return 0;

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert afq.abi_version() == 2
+    assert afq.abi_version() == 3
     for st in range(0, -9, -1):
         s = afq.status_string(st)
         assert s and s != "unknown status"
@@ -186,6 +186,58 @@ def test_act_and_quant_validation_errors():
     assert lib.fp8_quant(ctypes.byref(q), None) == -7
     q.dtype, q.cols = 2, 100
     assert lib.fp8_quant(ctypes.byref(q), None) == -2
+
+
+def test_copy_only_validation():
+    """values and scales both NULL: a copy-only launch (the first kernel of
+    an unfused chain).  Its copy is required, its widths need only be whole
+    chunks, it reads the default input only, and one of values / scales
+    alone is a NULL error."""
+    lib = afq.load()
+
+    def copy_only(**kw):
+        d = _norm(**kw)
+        d.seg[0].out.values, d.seg[0].out.scales, d.seg[0].out.normed = None, None, A16 * 3
+        return d
+
+    assert _call_norm(copy_only(M=0, cols=48)) == 0             # width 48: no 1x32 groups needed
+    assert _call_norm(copy_only(M=0, cols=44)) == -2            # still whole 8-element chunks
+    assert _call_norm(copy_only(quant_input=afq.QIN_FP32, mode=afq.BLOCK128)) == -6
+    d = copy_only()
+    d.seg[0].out.normed = None                                  # nothing to write
+    assert _call_norm(d) == -1
+    d = copy_only()
+    d.seg[0].out.scales = A16 * 4                               # scales without codes
+    assert _call_norm(d) == -1
+    d = copy_only()
+    d.seg[0].out.normed = A16 * 3 + 8                           # misaligned copy
+    assert _call_norm(d) == -3
+    d = copy_only()
+    d.seg[0].out.normed = A16                                   # copy over the input
+    assert _call_norm(d) == -5
+    d = copy_only(nseg=2)                                       # one segment quantised, one not
+    d.seg[1] = d.seg[0]
+    d.seg[1].x, d.seg[1].weight = A16 * 16, A16 * 17
+    d.seg[1].out.values, d.seg[1].out.scales, d.seg[1].out.normed = A16 * 18, A16 * 19, A16 * 20
+    assert _call_norm(d) == -1
+    a = afq._ActDesc()
+    a.M, a.I, a.gate_up, a.gate_up_row_stride, a.mode = 0, 200, A16, 400, afq.BLOCK128
+    a.out.normed = A16 * 64
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == 0      # 200 % 128 != 0: fine without groups
+    a.M = 4
+    a.quant_input = afq.QIN_BF16
+    a.mode = afq.MXFP8
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == -6     # bf16-first: a quantiser input
+    a.quant_input = afq.QIN_DEFAULT
+    a.out.normed = None
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == -1
+    a.out.normed, a.out.values = A16 * 64, A16 * 128
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == -2     # quantising: 200 is no 1x32 width
+    a.I, a.gate_up_row_stride = 256, 512
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == -1     # codes without scales
+    a.out.values = None
+    a.mode = afq.PER_TOKEN
+    assert lib.silu_mul_quant(ctypes.byref(a), None) == -6     # no per-token activation
 
 
 def test_binding_refuses_without_library(monkeypatch):

@@ -331,6 +331,85 @@ def test_fused_silu_b128_equals_silu_then_quant():
                           scales_u8_or_f32(sep.scales).view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_unfused_norm_chain_equals_fused(mode, dtype):
+    """The unfused chain on this library's kernels -- a copy-only norm launch,
+    then fp8_quant of its rows -- equals the fused launch bit for bit:
+    residual, normed rows, codes and scales ([P1] "Test Plan /
+    Correctness" states this of the fused MXFP8 norm)."""
+    M, H = 37, 6144
+    d = inputs.norm_inputs(M, H, seed=31, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1,
+                           dtype=dtype)
+    x, w, r = dev16(d["x"], dtype), dev16(d["w"], dtype), dev16(d["r"], dtype)
+    fused = afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=MODE[mode], kind=afq.GEMMA, residual=r,
+                                        want_normed=True)
+    plain = afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=MODE[mode], kind=afq.GEMMA, residual=r,
+                                        quantize=False)
+    assert plain.values is None and plain.scales is None
+    q = afq.fp8_quant(plain.normed, MODE[mode])
+    torch.cuda.synchronize()
+    assert torch.equal(plain.residual, fused.residual)
+    assert torch.equal(plain.normed.view(torch.int16), fused.normed.view(torch.int16))
+    assert torch.equal(q.values.view(torch.uint8), fused.values.view(torch.uint8))
+    assert torch.equal(q.scales.view(torch.uint8), fused.scales.view(torch.uint8))
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode, dtype=dtype)
+    check_dtype16(host16(plain.normed), ref["normed"], f"copy-only {mode} {dtype}")
+
+
+def test_copy_only_norm_odd_width_and_two_segments():
+    """A copy-only launch needs no quantisation groups (width 200 = 25
+    chunks), and a two-segment copy-only launch writes both segments' rows."""
+    d = inputs.norm_inputs(11, 200, seed=33, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
+    plain = afq.fused_add_rmsnorm_quant(dev16(d["x"]), dev16(d["w"]), 1e-6, mode=afq.PER_TOKEN,
+                                        kind=afq.STANDARD, residual=dev16(d["r"]), quantize=False)
+    torch.cuda.synchronize()
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="pt")
+    check_dtype16(host16(plain.residual), ref["h"], "copy-only w200 h", exact=True)
+    check_dtype16(host16(plain.normed), ref["normed"], "copy-only w200")
+    segs = inputs.two_segment_inputs(9, (1536, 512), seed=34)
+    xs = [dev16(sg["x"]) for sg in segs]
+    ws = [dev16(sg["w"]) for sg in segs]
+    fused = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=afq.PER_TOKEN, kind=afq.STANDARD,
+                                        want_normed=True)
+    plain = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=afq.PER_TOKEN, kind=afq.STANDARD,
+                                        quantize=False)
+    torch.cuda.synchronize()
+    for f, p in zip(fused, plain):
+        assert p.values is None and torch.equal(p.normed.view(torch.int16), f.normed.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode,I", [("mx", 768), ("b128", 3072)])
+def test_unfused_silu_chain(mode, I):
+    """The unfused SiLU chain on this library's kernels -- a copy-only
+    SiLU-and-mul launch, then fp8_quant of its bf16 activation.  1x128: equal
+    to the fused launch bit for bit ([P2] "Modifications").  MXFP8: equal to
+    the fused bf16-first variant bit for bit; the default MXFP8 fusion
+    quantises the fp32 activation instead, so a few % of its codes differ
+    ([P1] "Test Plan / Correctness")."""
+    gu = inputs.gate_up_inputs(29, I, seed=32, std=2.0)
+    g = dev16(gu)
+    fused = afq.silu_mul_quant(g, MODE[mode], want_act=True)
+    plain = afq.silu_mul_quant(g, MODE[mode], quantize=False)
+    assert plain.values is None and plain.scales is None
+    q = afq.fp8_quant(plain.normed, MODE[mode])
+    torch.cuda.synchronize()
+    assert torch.equal(plain.normed.view(torch.int16), fused.normed.view(torch.int16))
+    ref = orc.silu_quant(gu, MODE[mode], threads=8)
+    check_dtype16(host16(plain.normed), ref["act"], f"copy-only silu {mode}", exact=(mode == "b128"))
+    if mode == "b128":
+        assert torch.equal(q.values.view(torch.uint8), fused.values.view(torch.uint8))
+        assert torch.equal(q.scales.view(torch.uint8), fused.scales.view(torch.uint8))
+    else:
+        bf = afq.silu_mul_quant(g, afq.MXFP8, quant_input=afq.QIN_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(q.values.view(torch.uint8), bf.values.view(torch.uint8))
+        assert torch.equal(q.scales, bf.scales)
+        differ = (q.values.view(torch.uint8) != fused.values.view(torch.uint8)).float().mean().item()
+        _report(f"silu mx: unfused chain vs fp32 fusion", dict(codes_differ=round(differ, 4)))
+        assert differ < 0.1
+
+
 def test_e4m3_conversion_structured_fp32():
     """Every fp32 exponent that reaches e4m3 (codes 0..448), all 2^5 top
     mantissa patterns times boundary low bits, both signs: quantised with
