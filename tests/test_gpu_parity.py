@@ -164,6 +164,29 @@ def test_two_segment_other_modes():
             check_norm(gpu, ref, mode, "bf16", f"two-seg-{mode}")
 
 
+@pytest.mark.parametrize("mode,widths,qin", [("pt", (1000, 512), 0), ("pt", (8, 2040), 0),
+                                             ("mx", (1568, 512), 0), ("b128", (1664, 384), 0),
+                                             ("pt", (1000, 512), 1), ("b128", (1664, 384), 1)])
+@pytest.mark.parametrize("M", [7, 1100])
+def test_two_segment_unaligned_boundary(mode, widths, qin, M):
+    """Two segments whose boundary is not on a 64-chunk line (the first
+    segment's chunk count is not a multiple of 64, down to a single chunk),
+    so the segment of each chunk is chosen per lane; at a decode row count
+    and at the bandwidth-bound row shape, with the default and the
+    fp32-direct quantiser input."""
+    segs = inputs.two_segment_inputs(M, widths, seed=41)
+    xs = [dev16(sg["x"]) for sg in segs]
+    ws = [dev16(sg["w"]) for sg in segs]
+    outs = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=MODE[mode], kind=afq.STANDARD,
+                                       want_normed=True, quant_input=qin)
+    torch.cuda.synchronize()
+    for sg, qa in zip(segs, outs):
+        gpu = dict(normed=host16(qa.normed), values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
+        ref = ref_norm(sg["x"], sg["w"], kind="standard", mode=mode, qin=qin)
+        name = f"two-seg {widths} {mode} qin={qin} M={M}"
+        _report(name, check_norm(gpu, ref, mode, "bf16", name, requant=(qin == 0)))
+
+
 # ----------------------------------------------------------- SiLU-and-mul
 def _run_silu(gu, mode):
     qa = afq.silu_mul_quant(dev16(gu), MODE[mode], want_act=True)
