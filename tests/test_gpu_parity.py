@@ -42,7 +42,7 @@ def test_norm_modes(mode, kind, dtype, H, M):
     _report(f"{mode}-{kind}-{dtype} H={H} M={M}", check_norm(gpu, ref, mode, dtype, "norm"))
 
 
-@pytest.mark.parametrize("H", [2176, 7168, 12288, 32768, 128, 8])
+@pytest.mark.parametrize("H", [2176, 7168, 12288, 20480, 24576, 32768, 128, 8])
 def test_norm_widths(H):
     mode = "b128" if H % 128 == 0 else "pt"
     d = inputs.norm_inputs(7, H, seed=4, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
@@ -125,6 +125,18 @@ def test_norm_bandwidth_row_counts(mode, H):
     gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
     ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
     _report(f"bandwidth rows {mode} H={H}", check_norm(gpu, ref, mode, "bf16", f"bw-{mode}"))
+
+
+@pytest.mark.parametrize("H", [20480, 32768])
+def test_per_token_wide_rows_bandwidth_shape(H):
+    """Per-token rows above 1024 rows take at least two chunks per lane, and
+    wide rows more (three at 20480, four at 32768): 1030 rows, every row
+    against the oracle, fp16."""
+    d = inputs.norm_inputs(1030, H, seed=42, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5,
+                           dtype="fp16")
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="pt", dtype="fp16")
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="standard", mode="pt", dtype="fp16")
+    _report(f"per-token wide H={H}", check_norm(gpu, ref, "pt", "fp16", f"pt-wide{H}"))
 
 
 @pytest.mark.parametrize("M,sampled", [(2048, False), (8192, True)])
