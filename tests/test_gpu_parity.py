@@ -335,6 +335,29 @@ def test_fp8_quant_standalone(dtype, mode):
         assert np.array_equal(gs.view(np.uint32), s.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("n", [3072, 20480, 32768])
+def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
+    """The standalone per-token quantiser above 1024 rows (two chunks per
+    lane, three at 20480, four at 32768): 1100 rows, bit-exact."""
+    rng = np.random.default_rng(11)
+    M = 1100
+    x = rng.standard_normal((M, n)) * 2.0 ** rng.integers(-8, 8, (M, 1))
+    if dtype == "fp32":
+        xh = x.astype(np.float32)
+        xt = torch.from_numpy(xh).cuda()
+        odt = orc.FP32
+    else:
+        xh = inputs.to_bits(x, dtype)
+        xt = dev16(xh, dtype)
+        odt = ORC_DT[dtype]
+    qa = afq.fp8_quant(xt, afq.PER_TOKEN)
+    torch.cuda.synchronize()
+    q, s = orc.quant(xh, odt, afq.PER_TOKEN, threads=8)
+    assert np.array_equal(host8(qa.values), q)
+    assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint32), s.view(np.uint32))
+
+
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_fused_norm_equals_norm_then_quant(mode, dtype):
