@@ -53,9 +53,12 @@
  * pull request 65478, "Test Plan / Correctness").
  *
  * SiLU-and-mul (silu_mul_quant), per element j of a row:
- *   MXFP8:    a_j = fp32(silu(gate_j) * up_j), quantised without any bf16
- *             rounding (vLLM pull request 65478, "Purpose", commit 2: the
- *             activation stays fp32 between SiLU-and-mul and the quantiser)
+ *   MXFP8:    a_j = fp32(fp32(silu(gate_j)) * up_j) -- SiLU-and-mul in fp32
+ *             arithmetic -- quantised without any bf16 rounding (vLLM pull
+ *             request 65478, "Purpose", commit 2: the activation stays fp32
+ *             between SiLU-and-mul and the quantiser).  The kernel's fp32
+ *             silu is within 2 ulp of fp32(silu) for gates >= -80, and
+ *             rounded to fp32 from an fp64 evaluation below.
  *   BLOCK128: a_j = bf16(bf16(silu(gate_j)) * up_j), the rounding of the
  *             unfused SiluAndMul, so the codes equal the unfused chain
  *             (SGLang pull request 48043, "Modifications")

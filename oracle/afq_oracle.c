@@ -421,10 +421,14 @@ double orc_silu(double g)
  * [gate | up], gate in columns [0, I), up in [I, 2I) ([P1] swiglu "split"
  * layout).
  *
- * MXFP8 ([P1] "Purpose", commit 2 and "Test Plan": the fused kernel takes
- * the fp32 activation straight into the quantiser, with no bf16 rounding):
- *     a_j = fl32(silu(g_j) * u_j)    (exact product rounded once to fp32)
+ * MXFP8 ([P1] "Purpose", commit 2 and "Test Plan": the SiLU-and-mul is
+ * evaluated in fp32 and its fp32 result goes straight into the quantiser,
+ * with no bf16 rounding).  In fp32 arithmetic silu is an fp32 value before
+ * it multiplies up, so:
+ *     s_j = fl32(silu(g_j)),  a_j = fl32(s_j * u_j)
  *     scale from the fp32 block amax, codes e4m3(clamp(a_j / X)).
+ * (For g below about -87, silu(g) is an fp32 subnormal or zero, and so is
+ * a_j unless |u_j| is large.)
  * BLOCK128 ([P2] "Modifications": the fused kernel takes the same two bf16
  * roundings as the unfused SiLU-and-mul, silu first and then the product,
  * so its output equals the unfused path):
@@ -452,11 +456,11 @@ int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_str
             double shi, slo, a;
             silu_2(g, &shi, &slo);
             if (mode == ORC_MXFP8) {
-                /* fp32 of silu(g) * u: the product of the leading term with
-                 * the bf16 u and its exact error (fma), plus the tail */
-                double p = shi * u;
-                double pe = fma(shi, u, -p) + slo * u;
-                a = (double)round_f32_2(p, pe);
+                /* s = fl32(silu(g)) from the two-term value; s * u of a
+                 * 24-bit and an 8-bit significand is exact in fp64, so one
+                 * more rounding gives fl32(s * u) */
+                double s32 = (double)round_f32_2(shi, slo);
+                a = (double)round_f32_2(s32 * u, 0.0);
             } else {
                 double sg = orc_decode_bf16(round_bf16_2(shi, slo));
                 a = orc_decode_bf16(orc_round_bf16(sg * u)); /* sg*u exact in fp64 */

@@ -307,6 +307,28 @@ def test_silu_mx_extreme_gates():
     check_scales(gpu["scales"], ref["scales"], 0, "silu-mx-extreme")
 
 
+def test_silu_mx_all_gates():
+    """MXFP8 SiLU-and-mul for every finite bf16 gate times eight up values
+    across the exponent range (1, -2.75, 2^-10, 3e-3, 96, -2^40, 2^-100,
+    1e30): the bf16 copy of the fp32 activation within 1 ulp of the oracle's
+    (the kernel's silu is within 2 fp32 ulp), codes and scales within the
+    budget, and the codes equal to the oracle quantiser applied to the
+    kernel's own activation."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    gates = c[((c >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    pad = (-gates.size) % 128
+    g = np.concatenate([gates, np.zeros(pad, np.uint16)]).reshape(-1, 128)
+    ups = inputs.to_bits(np.array([1.0, -2.75, 2.0 ** -10, 3e-3, 96.0, -(2.0 ** 40), 2.0 ** -100, 1e30]))
+    gu = np.concatenate([np.concatenate([g, np.full_like(g, u)], axis=1) for u in ups], axis=0)
+    gpu = _run_silu(gu, "mx")
+    ref = orc.silu_quant(gu, orc.MXFP8, threads=8)
+    n_act = check_dtype16(gpu["act"], ref["act"], "silu-mx all gates act")
+    n_codes = check_codes(gpu["values"], ref["values"], "silu-mx all gates")
+    n_sc = check_scales(gpu["scales"], ref["scales"], 0, "silu-mx all gates")
+    _report("silu-mx all gates x 8 ups", dict(elements=int(gu.shape[0] * 128), act_1ulp=n_act,
+                                               codes_1=n_codes, scales_bad=n_sc))
+
+
 # --------------------------------------------------------- standalone quant
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])

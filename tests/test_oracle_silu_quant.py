@@ -52,33 +52,42 @@ def test_silu_bf16_rounding_exhaustive():
     assert not bad, bad[:10]
 
 
+def _silu_fp32_act(gb, ub):
+    """fl32(fl32(silu(g)) * u) from 60-digit silu and exact roundings (the
+    fp32 SiLU-and-mul of the MXFP8 path)."""
+    gf = brute.frac_of_bits16(gb, "bf16")
+    uf = brute.frac_of_bits16(ub, "bf16")
+    a = brute.rn_f32(brute.rn_f32(_silu_exact(gf)) * uf)
+    if a == 0:  # a zero keeps the IEEE sign of the product (silu(g) has the sign of g)
+        return Decimal("-0") if ((int(gb) ^ int(ub)) >> 15) & 1 else Decimal(0)
+    return a
+
+
 def test_silu_fp32_product_brute_force():
-    """MXFP8 activation: fp32 of silu(g) * u (one rounding), checked with
-    decimal arithmetic on random bf16 pairs (incl. large |g|)."""
+    """MXFP8 activation: fl32(fl32(silu(g)) * u), checked with decimal silu
+    and exact roundings on random bf16 pairs (incl. large |g|), and on gates
+    whose silu is an fp32 subnormal or zero times large up values, where
+    rounding silu to fp32 first decides the result."""
     rng = np.random.default_rng(21)
     I = 256
     g = rng.standard_normal(I) * 4.0
     g[:8] = [-95.0, -88.5, -60.0, -20.0, 20.0, 60.0, 0.0, -1e-30]
-    gu = np.concatenate([inputs.to_bits(g), inputs.to_bits(rng.standard_normal(I) * 2.0)])[None, :]
+    u = rng.standard_normal(I) * 2.0
+    g[8:16] = [-95.0, -100.0, -103.0, -109.0, -118.0, -90.0, -87.5, -150.0]
+    u[8:16] = [1e30, -(2.0 ** 40), 1e30, 1e30, 1e30, 2.0 ** 100, 2.0 ** 60, 1e38]
+    gu = np.concatenate([inputs.to_bits(g), inputs.to_bits(u)])[None, :]
     out = orc.silu_quant(gu, orc.MXFP8)
     act = out["act"][0]
     for j in range(I):
-        gf = brute.frac_of_bits16(gu[0, j], "bf16")
-        uf = brute.frac_of_bits16(gu[0, I + j], "bf16")
-        a = _silu_exact(gf) * (Decimal(uf.numerator) / Decimal(uf.denominator))
-        a32 = np.float32(float(a))  # decimal -> double -> float: one rounding is safe here
-        c, _ = brute.round16(Decimal(float(a32)), "bf16")
+        c, _ = brute.round16(_silu_fp32_act(gu[0, j], gu[0, I + j]), "bf16")
         assert c == int(act[j]), j
+    # fl32(silu(-109)) is -0, so the product is -0 whatever up is
+    assert int(act[11]) == 0x8000
 
 
 def _silu_mx_row_brute(gbits, ubits):
     """Exact activation of one row then the MX quantiser of the brute force."""
-    a = []
-    for gb, ub in zip(gbits, ubits):
-        gf = brute.frac_of_bits16(gb, "bf16")
-        uf = brute.frac_of_bits16(ub, "bf16")
-        v = _silu_exact(gf) * (Decimal(uf.numerator) / Decimal(uf.denominator))
-        a.append(Fraction(float(np.float32(float(v)))))
+    a = [_silu_fp32_act(gb, ub) for gb, ub in zip(gbits, ubits)]
     codes, scales = [], []
     for k in range(0, len(a), 32):
         q, s = brute.quant_mx(a[k:k + 32])
@@ -119,19 +128,16 @@ def test_silu_quant_matches_brute_force(mode):
 
 
 def test_silu_mx_bf16_first_matches_brute_force():
-    """The bf16-first MXFP8 variant quantises RNE_bf16(fl32(silu(g) u)), the
-    activation as the unfused chain stores it (decimal silu, exact roundings,
-    brute-force MX quantiser)."""
+    """The bf16-first MXFP8 variant quantises RNE_bf16(fl32(fl32(silu(g)) u)),
+    the activation as the unfused chain stores it (decimal silu, exact
+    roundings, brute-force MX quantiser)."""
     I = 256
     gu = inputs.gate_up_inputs(2, I, seed=23, std=2.0)
     out = orc.silu_quant(gu, orc.MXFP8, qin=orc.QIN_BF16)
     for i in range(2):
         a = []
         for gb, ub in zip(gu[i, :I], gu[i, I:]):
-            gf = brute.frac_of_bits16(gb, "bf16")
-            uf = brute.frac_of_bits16(ub, "bf16")
-            v = _silu_exact(gf) * (Decimal(uf.numerator) / Decimal(uf.denominator))
-            _, ab = brute.round16(brute.rn_f32(v), "bf16")
+            _, ab = brute.round16(_silu_fp32_act(gb, ub), "bf16")
             a.append(ab)
         codes, scales = [], []
         for k in range(0, I, 32):
