@@ -83,7 +83,10 @@
  *     M == 0 returns AFQ_OK after the shape checks and enqueues nothing.
  *   - Overlap between buffers is judged on each buffer's byte span from its
  *     first to its last byte.
- *   - Inputs are assumed finite; NaN or Inf inputs give unspecified codes.
+ *   - Inputs are assumed finite, and so is the rounded residual sum
+ *     round_dt(x + r) (fp16 overflows above 65504); otherwise the outputs
+ *     are unspecified (no error is reported and nothing outside the outputs
+ *     is written).
  *
  * Copy-only launches (ABI 3): when out.values and out.scales are both NULL
  * (in every segment of a norm launch), fused_add_rmsnorm_quant and
