@@ -86,7 +86,10 @@
  *   - Inputs are assumed finite, and so is the rounded residual sum
  *     round_dt(x + r) (fp16 overflows above 65504); otherwise the outputs
  *     are unspecified (no error is reported and nothing outside the outputs
- *     is written).
+ *     is written).  The mean square is accumulated in fp32, so the same
+ *     holds for rows whose sum of squares overflows fp32 (|h| above about
+ *     1e19 / sqrt(cols)) and for mean(h^2) + eps == 0 (eps = 0 with an
+ *     all-zero row).
  *
  * Copy-only launches (ABI 3): when out.values and out.scales are both NULL
  * (in every segment of a norm launch), fused_add_rmsnorm_quant and
