@@ -558,8 +558,8 @@ def main():
                          "(for rocprofv3 trace and counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the fused kernels are row-independent and this build "
-              "has no multi-GPU path (see DESIGN.md on sharding); run with --gpus 1",
+        print("bench.py measures one GPU: rows are independent and the library has no "
+              "multi-GPU path (a row-sharded launch per GPU needs no exchange); run with --gpus 1",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
