@@ -89,7 +89,9 @@
  *     is written).  The mean square is accumulated in fp32, so the same
  *     holds for rows whose sum of squares overflows fp32 (|h| above about
  *     1e19 / sqrt(cols)) and for mean(h^2) + eps == 0 (eps = 0 with an
- *     all-zero row).
+ *     all-zero row); and, for SiLU-and-mul, for a quantisation group whose
+ *     activation overflows its dtype (|silu(gate) * up| beyond the fp32 or
+ *     bf16 range).
  *
  * Copy-only launches (ABI 3): when out.values and out.scales are both NULL
  * (in every segment of a norm launch), fused_add_rmsnorm_quant and

@@ -307,6 +307,33 @@ def test_silu_mx_extreme_gates():
     check_scales(gpu["scales"], ref["scales"], 0, "silu-mx-extreme")
 
 
+def test_silu_b128_all_gates_many_ups():
+    """1x128 SiLU-and-mul for every finite bf16 gate times seven up values
+    (-2.75, 2^-10, 3e-3, 96, -2^40, 2^-100, 1e20): the activation
+    bit-identical to the oracle (the path's arithmetic is exact: bf16(silu),
+    an exact product, one rounding), and the codes and scales of every group
+    whose activation stays finite too (an activation that overflows the bf16
+    range leaves its group's outputs unspecified)."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    gates = c[((c >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    pad = (-gates.size) % 128
+    g = np.concatenate([gates, np.zeros(pad, np.uint16)]).reshape(-1, 128)
+    ups = inputs.to_bits(np.array([-2.75, 2.0 ** -10, 3e-3, 96.0, -(2.0 ** 40), 2.0 ** -100, 1e20]))
+    gu = np.concatenate([np.concatenate([g, np.full_like(g, u)], axis=1) for u in ups], axis=0)
+    gpu = _run_silu(gu, "b128")
+    ref = orc.silu_quant(gu, orc.BLOCK128, threads=8)
+    bad = np.flatnonzero(gpu["act"].ravel() != ref["act"].ravel())
+    assert bad.size == 0, [(hex(int(gu.ravel()[0])), int(i)) for i in bad[:5]]
+    # groups whose activation overflows (silu(g) * up beyond the bf16 range)
+    # have unspecified codes and scales; every other group is bit-exact
+    inf = (ref["act"] & 0x7FFF) == 0x7F80
+    ok = ~inf.reshape(gu.shape[0], -1, 128).any(axis=2)          # [rows, groups]
+    assert np.array_equal(gpu["scales"].view(np.uint32)[ok], ref["scales"].view(np.uint32)[ok])
+    okel = np.repeat(ok, 128, axis=1)
+    assert np.array_equal(gpu["values"][okel], ref["values"][okel])
+    _report("silu-b128 all gates x 7 ups", dict(groups=int(ok.size), overflowing_groups=int((~ok).sum())))
+
+
 def test_silu_mx_all_gates():
     """MXFP8 SiLU-and-mul for every finite bf16 gate times eight up values
     across the exponent range (1, -2.75, 2^-10, 3e-3, 96, -2^40, 2^-100,
