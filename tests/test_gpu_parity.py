@@ -410,6 +410,35 @@ def test_fp8_quant_mx_every_bf16_value_under_every_block_exponent():
     assert bad.size == 0, [(int(x[tuple(b)]), int(host8(qa.values)[tuple(b)]), int(q[tuple(b)])) for b in bad[:5]]
 
 
+def test_fp8_quant_mx_every_fp16_value_under_every_block_exponent():
+    """The same sweep for fp16 input: every finite fp16 value u under every
+    block exponent that admits it (fp16 subnormals are normal in fp32, so
+    the block exponents are taken from the fp32 exponent field of the
+    decoded values), bit-identical to the oracle."""
+    c = np.arange(1 << 16, dtype=np.uint32)
+    fin = c[((c >> 10) & 0x1F) != 0x1F].astype(np.uint16)
+    val = fin.view(np.float16).astype(np.float32)
+    field = (val.view(np.uint32) >> 23) & 0xFF                  # 0 only for +-0
+    pos = fin[(fin & 0x8000) == 0]
+    pos_field = (pos.view(np.float16).astype(np.float32).view(np.uint32) >> 23) & 0xFF
+    blocks = []
+    for E in np.unique(pos_field[pos_field > 0]):
+        amax = pos[pos_field == E].max()                         # largest fp16 of this exponent
+        vals = fin[field <= E]
+        n = -(-vals.size // 31)
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:vals.size] = vals
+        blocks.append(np.concatenate([np.full((n, 1), amax, np.uint16), pad.reshape(n, 31)], axis=1))
+    x = np.concatenate(blocks)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 192, 32), np.uint16)]).reshape(-1, 6144)
+    qa = afq.fp8_quant(dev16(x, "fp16"), afq.MXFP8)
+    torch.cuda.synchronize()
+    q, sc = orc.quant(x, orc.FP16, orc.MXFP8, threads=8)
+    assert np.array_equal(scales_u8_or_f32(qa.scales), sc)
+    assert np.array_equal(host8(qa.values), q)
+    _report("mx quant every fp16 value", dict(elements=int(x.size), block_exponents=len(blocks)))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("n", [3072, 20480, 32768])
 def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
