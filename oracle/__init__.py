@@ -82,6 +82,13 @@ def lib():
                                               F32, P, P, P, I64, I64, P]
             L.orc_silu_quant_rows.restype = I32
             L.orc_silu_quant_rows.argtypes = [I64, I64, P, I64, I32, I32, P, P, P, I64, I64, P]
+            L.orc_swiglu_glu32_n.restype = None
+            L.orc_swiglu_glu32_n.argtypes = [P, P, I64, F32, F32]
+            L.orc_swiglu_act32_n.restype = None
+            L.orc_swiglu_act32_n.argtypes = [P, P, P, I64, F32, F32, F32]
+            L.orc_swiglu_oai_quant_rows.restype = I32
+            L.orc_swiglu_oai_quant_rows.argtypes = [I64, I64, P, I64, I32, I32, F32, F32, F32,
+                                                    P, P, P, I64, I64, P]
             _lib = L
     return _lib
 
@@ -145,6 +152,26 @@ def silu(g) -> np.ndarray:
     g = np.ascontiguousarray(g, dtype=np.float64)
     out = np.empty(g.shape, np.float64)
     lib().orc_silu_n(_ptr(g), _ptr(out), g.size)
+    return out
+
+
+def swiglu_glu32(g, alpha: float, limit: float) -> np.ndarray:
+    """fl32(min(g, limit) * logistic(alpha * min(g, limit))), alpha and limit
+    taken as fp32 values: the gate factor of the clamped SwiGLU."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    out = np.empty(g.shape, np.float32)
+    lib().orc_swiglu_glu32_n(_ptr(g), _ptr(out), g.size, float(alpha), float(limit))
+    return out
+
+
+def swiglu_act32(g, u, alpha: float, beta: float, limit: float) -> np.ndarray:
+    """The fp32 clamped-SwiGLU activation fl32(glu32 * fl32(clamp(u) + beta))."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    assert g.shape == u.shape
+    out = np.empty(g.shape, np.float32)
+    lib().orc_swiglu_act32_n(_ptr(g), _ptr(u), _ptr(out), g.size, float(alpha), float(beta),
+                             float(limit))
     return out
 
 
@@ -248,6 +275,37 @@ def silu_quant(gu, mode: int, *, want_act: bool = True, threads: int = 1, rows=N
                                        _ptr(scales), _ptr(act), r0, r1, _ptr(work))
         if rc != 0:
             raise ValueError("oracle: SiLU-and-mul supports the MXFP8 and 1x128 modes")
+
+    if rows is None:
+        _parallel_rows(M, threads, run_range)
+    else:
+        for r in np.asarray(rows, dtype=np.int64):
+            run_range(int(r), int(r) + 1)
+    return dict(values=values, scales=scales, act=act)
+
+
+def swiglu_oai_quant(gu, alpha: float, beta: float, limit: float, mode: int = MXFP8, *,
+                     want_act: bool = True, threads: int = 1, rows=None,
+                     qin: int = QIN_DEFAULT):
+    """Clamped SwiGLU + MXFP8 quantisation of gu [M, 2I] bf16 ([gate | up]):
+    a = fl32(fl32(glu) * fl32(clamp(up, +-limit) + beta)), glu =
+    min(gate, limit) * logistic(alpha * min(gate, limit)).  qin = QIN_BF16
+    quantises the bf16-rounded activation (the unfused chain's input)."""
+    gu = np.ascontiguousarray(gu, dtype=np.uint16)
+    M, two_i = gu.shape
+    assert two_i % 2 == 0
+    I = two_i // 2
+    values = np.zeros((M, I), np.uint8)
+    scales = _scales_array(M, I, mode)
+    act = np.zeros((M, I), np.uint16) if want_act else None
+
+    def run_range(r0, r1):
+        work = np.empty(max(I, 1), np.float64)
+        rc = lib().orc_swiglu_oai_quant_rows(M, I, _ptr(gu), two_i, mode, qin, float(alpha),
+                                             float(beta), float(limit), _ptr(values),
+                                             _ptr(scales), _ptr(act), r0, r1, _ptr(work))
+        if rc != 0:
+            raise ValueError("oracle: the clamped SwiGLU supports the MXFP8 mode only")
 
     if rows is None:
         _parallel_rows(M, threads, run_range)

@@ -476,6 +476,102 @@ int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_str
 }
 
 /* ------------------------------------------------------------------------ */
+/*
+ * Clamped SwiGLU ("swiglu_oai" in [P1]'s benchmark script, called there with
+ * alpha = 1.702, beta = 1.0, limit = 7.0 on the split [gate | up] layout).
+ * The pages name the function and its three parameters but do not write it
+ * out; the reading taken is the clamped SwiGLU published with OpenAI's
+ * gpt-oss models, per element:
+ *     gc  = min(g, limit)                    (gate clamped from above only)
+ *     uc  = min(max(u, -limit), limit)       (up clamped on both sides)
+ *     glu = gc * logistic(alpha * gc)
+ *     a   = glu * (uc + beta)
+ * MXFP8, fp32 arithmetic as in the SiLU path ([P1] "Purpose", commit 2: the
+ * swiglu is evaluated in fp32 and quantised in the same pass): each of glu,
+ * uc + beta and their product is rounded to fp32 once,
+ *     a_j = fl32(fl32(glu_j) * fl32(uc_j + beta)),
+ * with alpha, beta and limit taken as the fp32 values the caller passes.
+ * qin = ORC_QIN_BF16: the quantiser reads RNE_bf16(a_j), the activation as
+ * the unfused swiglu -> quant chain stores it ([P1] "Test Plan /
+ * Correctness").  act_out (optional) receives RNE_bf16(a_j).  Only MXFP8
+ * (returns -1 otherwise).
+ */
+
+/* glu = gc * logistic(z), z = alpha * gc, as a two-term value hi + lo.  For
+ * |z| < 1/2 it is written gc/2 + (gc/2) tanh(z/2) (logistic(z) = (1 +
+ * tanh(z/2)) / 2), so that for tiny gates the information beyond gc/2 is
+ * kept in the second term; otherwise gc e^z / (1 + e^z) (z < 0, no
+ * overflow) or gc / (1 + e^-z).  A zero gate keeps its sign. */
+static void glu_2(double gc, double z, double *hi, double *lo)
+{
+    *lo = 0.0;
+    if (gc == 0.0) {
+        *hi = gc;
+        return;
+    }
+    if (fabs(z) < 0.5) {
+        double a = gc / 2.0, b = (gc / 2.0) * tanh(z / 2.0);
+        double s = a + b;
+        *hi = s;
+        *lo = b - (s - a);   /* |a| >= |b|: exact error of the sum */
+        return;
+    }
+    if (z < 0.0) {
+        double e = exp(z);
+        *hi = gc * e / (1.0 + e);
+    } else {
+        *hi = gc / (1.0 + exp(-z));
+    }
+}
+
+/* fl32(glu) of a gate: gc = min(g, limit), alpha * gc exact in fp64 (a
+ * 24-bit times an at most 24-bit significand) */
+float orc_swiglu_glu32(double g, float alpha, float limit)
+{
+    double gc = g < (double)limit ? g : (double)limit;
+    double hi, lo;
+    glu_2(gc, (double)alpha * gc, &hi, &lo);
+    return round_f32_2(hi, lo);
+}
+
+/* The fp32 activation a = fl32(fl32(glu) * fl32(uc + beta)). */
+float orc_swiglu_act32(double g, double u, float alpha, float beta, float limit)
+{
+    double L = (double)limit, B = (double)beta;
+    double uc = u < -L ? -L : (u > L ? L : u);
+    double glu32 = (double)orc_swiglu_glu32(g, alpha, limit);
+    /* uc + beta with its exact error (two-sum), rounded once */
+    double s = uc + B, bb = s - uc;
+    double err = (uc - (s - bb)) + (B - bb);
+    double lin32 = (double)round_f32_2(s, err);
+    /* the product of two fp32 values is exact in fp64 */
+    return round_f32_2(glu32 * lin32, 0.0);
+}
+
+int orc_swiglu_oai_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
+                              int mode, int qin, float alpha, float beta, float limit,
+                              uint8_t *values, void *scales, uint16_t *act_out,
+                              int64_t r0, int64_t r1, double *work /* I doubles */)
+{
+    (void)M;
+    if (mode != ORC_MXFP8) return -1;
+    int64_t spr = scales_per_row(I, mode), sb = scale_bytes(mode);
+    for (int64_t i = r0; i < r1; ++i) {
+        const uint16_t *row = gu + i * gu_stride;
+        for (int64_t j = 0; j < I; ++j) {
+            double a = (double)orc_swiglu_act32(orc_decode_bf16(row[j]), orc_decode_bf16(row[I + j]),
+                                                alpha, beta, limit);
+            uint16_t ac = orc_round_bf16(a);
+            if (qin == ORC_QIN_BF16) a = orc_decode_bf16(ac);
+            work[j] = a;
+            if (act_out) act_out[i * I + j] = ac;
+        }
+        quant_row(work, I, mode, values + i * I, (uint8_t *)scales + i * spr * sb);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array helpers for the tests (element-wise application of the above).     */
 void orc_round_bf16_n(const double *v, uint16_t *out, int64_t n)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_round_bf16(v[i]); }
@@ -487,3 +583,8 @@ void orc_e8m0_byte_n(const float *a, uint8_t *out, int64_t n)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_e8m0_byte(a[i]); }
 void orc_silu_n(const double *g, double *out, int64_t n)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_silu(g[i]); }
+void orc_swiglu_glu32_n(const double *g, float *out, int64_t n, float alpha, float limit)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_swiglu_glu32(g[i], alpha, limit); }
+void orc_swiglu_act32_n(const double *g, const double *u, float *out, int64_t n, float alpha,
+                        float beta, float limit)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_swiglu_act32(g[i], u[i], alpha, beta, limit); }
