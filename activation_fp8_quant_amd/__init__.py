@@ -8,6 +8,7 @@ of the computation runs in the library's HIP kernels; there is no fallback.
 Entry points (same names as the C ABI):
     fused_add_rmsnorm_quant(x, weight, eps, ...)   residual add + RMSNorm + quant
     silu_mul_quant(gate_up, mode, ...)             SiLU-and-mul + quant
+    swiglu_oai_quant(gate_up, alpha, beta, limit)  clamped SwiGLU + MXFP8
     fp8_quant(x, mode, ...)                        standalone row-wise quant
 """
 from __future__ import annotations
@@ -23,7 +24,7 @@ __all__ = [
     "MXFP8", "BLOCK128", "PER_TOKEN", "STANDARD", "GEMMA",
     "QIN_DEFAULT", "QIN_FP32", "QIN_BF16",
     "QuantizedActivation", "AfqError",
-    "fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant",
+    "fused_add_rmsnorm_quant", "silu_mul_quant", "swiglu_oai_quant", "fp8_quant",
     "abi_version", "status_string", "library_path", "load",
 ]
 
@@ -75,6 +76,11 @@ class _ActDesc(ctypes.Structure):
                 ("quant_input", ctypes.c_int32), ("out", _QAct)]
 
 
+class _SwigluDesc(ctypes.Structure):
+    _fields_ = [("act", _ActDesc), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("limit", ctypes.c_float)]
+
+
 class _QuantDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("cols", ctypes.c_int64), ("x", ctypes.c_void_p),
                 ("x_row_stride", ctypes.c_int64), ("dtype", ctypes.c_int32),
@@ -95,7 +101,7 @@ def load():
             "`python -m activation_fp8_quant_amd.build` (there is no fallback path)")
     lib = ctypes.CDLL(library_path)
     for name, desc in (("fused_add_rmsnorm_quant", _NormDesc), ("silu_mul_quant", _ActDesc),
-                       ("fp8_quant", _QuantDesc)):
+                       ("swiglu_oai_quant", _SwigluDesc), ("fp8_quant", _QuantDesc)):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(desc), ctypes.c_void_p]
@@ -347,6 +353,25 @@ def fused_add_rmsnorm_quant(
     return results[0] if len(results) == 1 else results
 
 
+def _act_desc(gate_up, mode, want_act, quant_input, quantize, out):
+    """Checks, output allocation and the descriptor shared by the SiLU-and-mul
+    and clamped-SwiGLU entry points."""
+    _rowmajor(gate_up, "gate_up")
+    if gate_up.dtype != torch.bfloat16:
+        raise TypeError("gate_up must be bfloat16")
+    M, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    I = two_i // 2
+    values, scales, act = _alloc_out(mode, M, I, gate_up.device, torch.bfloat16, want_act, out,
+                                     quantize)
+    d = _ActDesc()
+    d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
+    d.quant_input = int(quant_input)
+    d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
+    return d, QuantizedActivation(values, scales, act, None, mode, gate_up.dtype, (M, I))
+
+
 def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
                    quant_input: int = QIN_DEFAULT, quantize: bool = True, out=None,
                    stream=None) -> QuantizedActivation:
@@ -361,23 +386,29 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
     """
     lib = load()
     mode = _mode(mode)
-    _rowmajor(gate_up, "gate_up")
-    if gate_up.dtype != torch.bfloat16:
-        raise TypeError("gate_up must be bfloat16")
-    M, two_i = gate_up.shape
-    if two_i % 2:
-        raise ValueError("gate_up must have an even number of columns")
-    I = two_i // 2
-    values, scales, act = _alloc_out(mode, M, I, gate_up.device, torch.bfloat16, want_act, out,
-                                     quantize)
-    d = _ActDesc()
-    d.M, d.I, d.gate_up, d.gate_up_row_stride, d.mode = M, I, gate_up.data_ptr(), gate_up.stride(0), mode
-    d.quant_input = int(quant_input)
-    d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), _ptr(act)
+    d, qa = _act_desc(gate_up, mode, want_act, quant_input, quantize, out)
     st = _launch(lib.silu_mul_quant, d, stream, gate_up.device)
     if st != 0:
         raise AfqError(st, "silu_mul_quant")
-    return QuantizedActivation(values, scales, act, None, mode, gate_up.dtype, (M, I))
+    return qa
+
+
+def swiglu_oai_quant(gate_up: torch.Tensor, alpha: float, beta: float, limit: float, *,
+                     want_act: bool = False, quant_input: int = QIN_DEFAULT,
+                     quantize: bool = True, out=None, stream=None) -> QuantizedActivation:
+    """Clamped SwiGLU of a bf16 [M, 2I] row ([gate | up]) + MXFP8:
+    a = fp32(glu) * fp32(clamp(up, +-limit) + beta), glu = gc * logistic(alpha
+    * gc), gc = min(gate, limit), quantised in fp32.  quant_input=QIN_BF16
+    quantises the bf16-rounded activation; quantize=False writes only the bf16
+    activation (the unfused chain's first kernel)."""
+    lib = load()
+    d, qa = _act_desc(gate_up, MXFP8, want_act, quant_input, quantize, out)
+    sd = _SwigluDesc()
+    sd.act, sd.alpha, sd.beta, sd.limit = d, float(alpha), float(beta), float(limit)
+    st = _launch(lib.swiglu_oai_quant, sd, stream, gate_up.device)
+    if st != 0:
+        raise AfqError(st, "swiglu_oai_quant")
+    return qa
 
 
 def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> QuantizedActivation:

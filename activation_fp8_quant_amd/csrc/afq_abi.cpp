@@ -97,6 +97,57 @@ int launched(int hip_err)
     return AFQ_OK;
 }
 
+// Checks and dispatch shared by the SiLU-and-mul and clamped-SwiGLU entry
+// points (act: 0 SiLU-and-mul, 1 clamped SwiGLU with its parameters in sw).
+int act_common(const afq_act_desc *d, int act, const afq_swiglu_desc *sw, void *stream)
+{
+    if (!valid_qin(d->quant_input)) return AFQ_ERR_ARG;
+    if (!valid_mode(d->mode)) return AFQ_ERR_ARG;
+    if (d->mode == AFQ_PER_TOKEN) return AFQ_ERR_UNSUPPORTED;
+    if (d->quant_input == AFQ_QIN_FP32) return AFQ_ERR_UNSUPPORTED;
+    if (d->quant_input == AFQ_QIN_BF16 && d->mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
+    // copy only (the SiLU-and-mul of the unfused chain): no codes or scales
+    const bool quant = d->out.values || d->out.scales;
+    if (!quant && d->quant_input != AFQ_QIN_DEFAULT) return AFQ_ERR_UNSUPPORTED;
+    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
+    if (!width_ok(d->I, d->mode, quant)) return AFQ_ERR_SHAPE;
+    if (!stride_ok(d->gate_up_row_stride, 2 * d->I)) return AFQ_ERR_SHAPE;
+    if (d->M == 0) return AFQ_OK;
+    if (!d->gate_up) return AFQ_ERR_NULL;
+    if (quant ? (!d->out.values || !d->out.scales) : !d->out.normed) return AFQ_ERR_NULL;
+    if (!aligned(d->gate_up, 16) || (d->gate_up_row_stride * 2) % 16 != 0) return AFQ_ERR_ALIGN;
+    if (quant && (!aligned(d->out.values, 16) || !aligned(d->out.scales, 4))) return AFQ_ERR_ALIGN;
+    if (d->out.normed && !aligned(d->out.normed, 16)) return AFQ_ERR_ALIGN;
+
+    const int64_t M = d->M, I = d->I;
+    Span outs[3] = {
+        span_of(d->out.values, M, I, 1, I),
+        span_of(d->out.scales, M, scale_cols(d->mode, I), scale_elt(d->mode),
+                scale_cols(d->mode, I) * scale_elt(d->mode)),
+        span_of(d->out.normed, M, I, 2, I * 2),
+    };
+    Span ins[1] = {span_of(d->gate_up, M, 2 * I, 2, d->gate_up_row_stride * 2)};
+    if (any_wraps(outs, 3) || any_wraps(ins, 1)) return AFQ_ERR_SHAPE;
+    if (any_overlap(outs, 3, ins, 1)) return AFQ_ERR_ALIAS;
+
+    afq::ActPlan p{};
+    p.gu = (const uint8_t *)d->gate_up;
+    p.gu_pitch = d->gate_up_row_stride * 2;
+    p.values = (uint8_t *)d->out.values;
+    p.scales = (uint8_t *)d->out.scales;
+    p.act = (uint8_t *)d->out.normed;
+    p.M = M;
+    p.I = (int32_t)I;
+    p.mode = d->mode;
+    p.qin = d->quant_input;
+    p.quant = quant ? 1 : 0;
+    p.act_kind = act;
+    p.alpha = sw ? sw->alpha : 1.0f;
+    p.beta = sw ? sw->beta : 0.0f;
+    p.limit = sw ? sw->limit : INFINITY;
+    return launched(afq::launch_act(p, stream));
+}
+
 } // namespace
 
 extern "C" {
@@ -226,47 +277,18 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *d, void *stream)
 int silu_mul_quant(const afq_act_desc *d, void *stream)
 {
     if (!d) return AFQ_ERR_NULL;
-    if (!valid_qin(d->quant_input)) return AFQ_ERR_ARG;
-    if (!valid_mode(d->mode)) return AFQ_ERR_ARG;
-    if (d->mode == AFQ_PER_TOKEN) return AFQ_ERR_UNSUPPORTED;
-    if (d->quant_input == AFQ_QIN_FP32) return AFQ_ERR_UNSUPPORTED;
-    if (d->quant_input == AFQ_QIN_BF16 && d->mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
-    // copy only (the SiLU-and-mul of the unfused chain): no codes or scales
-    const bool quant = d->out.values || d->out.scales;
-    if (!quant && d->quant_input != AFQ_QIN_DEFAULT) return AFQ_ERR_UNSUPPORTED;
-    if (!rows_ok(d->M)) return AFQ_ERR_SHAPE;
-    if (!width_ok(d->I, d->mode, quant)) return AFQ_ERR_SHAPE;
-    if (!stride_ok(d->gate_up_row_stride, 2 * d->I)) return AFQ_ERR_SHAPE;
-    if (d->M == 0) return AFQ_OK;
-    if (!d->gate_up) return AFQ_ERR_NULL;
-    if (quant ? (!d->out.values || !d->out.scales) : !d->out.normed) return AFQ_ERR_NULL;
-    if (!aligned(d->gate_up, 16) || (d->gate_up_row_stride * 2) % 16 != 0) return AFQ_ERR_ALIGN;
-    if (quant && (!aligned(d->out.values, 16) || !aligned(d->out.scales, 4))) return AFQ_ERR_ALIGN;
-    if (d->out.normed && !aligned(d->out.normed, 16)) return AFQ_ERR_ALIGN;
+    return act_common(d, 0, nullptr, stream);
+}
 
-    const int64_t M = d->M, I = d->I;
-    Span outs[3] = {
-        span_of(d->out.values, M, I, 1, I),
-        span_of(d->out.scales, M, scale_cols(d->mode, I), scale_elt(d->mode),
-                scale_cols(d->mode, I) * scale_elt(d->mode)),
-        span_of(d->out.normed, M, I, 2, I * 2),
-    };
-    Span ins[1] = {span_of(d->gate_up, M, 2 * I, 2, d->gate_up_row_stride * 2)};
-    if (any_wraps(outs, 3) || any_wraps(ins, 1)) return AFQ_ERR_SHAPE;
-    if (any_overlap(outs, 3, ins, 1)) return AFQ_ERR_ALIAS;
-
-    afq::ActPlan p{};
-    p.gu = (const uint8_t *)d->gate_up;
-    p.gu_pitch = d->gate_up_row_stride * 2;
-    p.values = (uint8_t *)d->out.values;
-    p.scales = (uint8_t *)d->out.scales;
-    p.act = (uint8_t *)d->out.normed;
-    p.M = M;
-    p.I = (int32_t)I;
-    p.mode = d->mode;
-    p.qin = d->quant_input;
-    p.quant = quant ? 1 : 0;
-    return launched(afq::launch_act(p, stream));
+int swiglu_oai_quant(const afq_swiglu_desc *d, void *stream)
+{
+    if (!d) return AFQ_ERR_NULL;
+    if (!std::isfinite(d->alpha) || !std::isfinite(d->beta) || std::isnan(d->limit) ||
+        !(d->limit > 0.0f))
+        return AFQ_ERR_ARG;
+    if (!valid_mode(d->act.mode)) return AFQ_ERR_ARG;
+    if (d->act.mode != AFQ_MXFP8) return AFQ_ERR_UNSUPPORTED;
+    return act_common(&d->act, 1, d, stream);
 }
 
 int fp8_quant(const afq_quant_desc *d, void *stream)

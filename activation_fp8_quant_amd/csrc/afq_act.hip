@@ -1,14 +1,21 @@
-// afq_act.hip -- SiLU-and-mul fused with FP8 quantisation.
+// afq_act.hip -- SiLU-and-mul and the clamped SwiGLU, fused with FP8
+// quantisation.
 //
-// act_quant_kernel works on a flat chunk index (8 activations per chunk):
-// a row has no cross-row work, so every lane is busy for any width I.
+// act_quant_kernel (SiLU-and-mul with MXFP8 or 1x128; the clamped SwiGLU
+// with MXFP8) works on a flat chunk index (8 activations per chunk): a row
+// has no cross-row work, so every lane is busy for any width I.
 // HBM-bound elementwise work: no dense contraction, so no MFMA.
 
 #include "afq_device.hpp"
 #include "afq_internal.h"
 #include "afq_launch.hpp"
 
+#include <cmath>
+
 namespace afq {
+
+// activation kinds
+constexpr int kSilu = 0, kSwigluOai = 1;
 
 struct ActArgs {
     const uint8_t *gu;
@@ -20,6 +27,10 @@ struct ActArgs {
     int32_t C;        // chunks per row (I / 8)
     int32_t I;
     DivC dc;          // division by C
+    // clamped SwiGLU only: alpha log2(e) = cHi + cLo with a 16-bit head
+    float alpha, beta, limit;
+    float cHi;        // alpha log2(e) to 16 significant bits
+    float cLoLn2;     // (alpha log2(e) - cHi) ln 2
 };
 
 // silu(g) = g / (1 + e^-g) in fp32 for a bf16 gate g >= -80, within 2 ulp
@@ -104,21 +115,96 @@ __device__ __forceinline__ void silu_bf16x8(const float (&g)[8], const uint4 &gb
     }
 }
 
-// fp32 silu of 8 gates for the MXFP8 path: the fast form; gates below -80
+// fp32 silu of N gates for the MXFP8 path: the fast form; gates below -80
 // (e^-g beyond the fp32 range) are redone in fp64.
-__device__ __forceinline__ void silu_f32x8(const float (&g)[8], float (&s)[8])
+template <int N>
+__device__ __forceinline__ void silu_f32xn(const float (&g)[N], float (&s)[N])
 {
     float gmin = g[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
         s[i] = silu_fast(g[i]);
         gmin = __builtin_fminf(gmin, g[i]);
     }
     if (gmin < -80.0f) {
 #pragma unroll 1
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < N; ++i)
             if (g[i] < -80.0f) s[i] = silu_f32_slow(g[i]);
     }
+}
+
+// Clamped SwiGLU, gate factor: glu = gc logistic(alpha gc) with gc =
+// min(g, limit), in fp32.  As in silu_fast, e^(-alpha gc) = 2^t e^y with
+// t = -cHi gc exact (a bf16 gc times a 16-bit head; for a limit that is not
+// a bf16 value a clamped gate makes t inexact by at most half an ulp) and
+// y = -cLo ln2 gc.  |cLo| <= 2^-16 |alpha log2(e)|, so |y| <= |t| 2^-16 ln2,
+// below 1.6e-3 wherever 2^t is not negligible (t > -150); e^y is taken to
+// second order (the cubic term is below 1e-9).  y is clamped to [-1, 1]
+// first, which changes nothing where it matters and keeps y^2 finite for
+// huge gates under an infinite limit (there 2^t is 0).  For alpha gc below
+// about -80 (t above 115, 2^t near the top of the fp32 range) the factor is
+// redone in fp64.
+__device__ __noinline__ float swiglu_glu_slow(float gc, float alpha)
+{
+    const double z = (double)alpha * (double)gc;
+    const double e = exp(z);
+    return (float)((double)gc * e / (1.0 + e));
+}
+
+template <int N>
+__device__ __forceinline__ void swiglu_act_xn(const ActArgs &a, const float (&g)[N], float (&v)[N])
+{
+    float glu[N];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float gc = __builtin_fminf(g[i], a.limit);
+        const float t = gc * -a.cHi;
+        const float y = __builtin_amdgcn_fmed3f(gc * -a.cLoLn2, -1.0f, 1.0f);
+        const float w = __builtin_fmaf(y, __builtin_fmaf(y, 0.5f, 1.0f), 1.0f);
+        const float d = __builtin_fmaf(__builtin_amdgcn_exp2f(t), w, 1.0f);
+        glu[i] = gc * __builtin_amdgcn_rcpf(d);
+        tmax = __builtin_fmaxf(tmax, t);
+    }
+    if (tmax > 115.0f) {
+#pragma unroll 1
+        for (int i = 0; i < N; ++i) {
+            const float gc = __builtin_fminf(g[i], a.limit);
+            if (gc * -a.cHi > 115.0f) glu[i] = swiglu_glu_slow(gc, a.alpha);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = glu[i] * (__builtin_amdgcn_fmed3f(v[i], -a.limit, a.limit) + a.beta);
+}
+
+// The fp32 activation of the MXFP8 path from the gates g and the up values
+// v (overwritten): SiLU-and-mul fl32(fl32(silu(g)) * up), or the clamped
+// SwiGLU fl32(glu * fl32(clamp(up, +-limit) + beta)).
+template <int ACT, int N>
+__device__ __forceinline__ void act_f32xn(const ActArgs &a, const float (&g)[N], float (&v)[N])
+{
+    if constexpr (ACT == kSwigluOai) {
+        swiglu_act_xn<N>(a, g, v);
+    } else {
+        float sg[N];
+        silu_f32xn<N>(g, sg);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] *= sg[i];
+    }
+}
+
+// 4 bf16 values of a packed 8-byte half chunk -> fp32, and back (RNE)
+__device__ __forceinline__ void unpack4(const uint2 &c, float (&v)[4])
+{
+    v[0] = bf16_lo(c.x);
+    v[1] = bf16_hi(c.x);
+    v[2] = bf16_lo(c.y);
+    v[3] = bf16_hi(c.y);
+}
+__device__ __forceinline__ uint2 pack4(const float (&v)[4])
+{
+    return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // The 1x128 outputs of one chunk from s = bf16(silu(gate)) and the up
@@ -140,12 +226,13 @@ __device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8],
     stg_stream(a.values + out_off, q);
 }
 
+// ACT: kSilu, or kSwigluOai (MXFP8 only: the clamped SwiGLU).
 // QBF16 (MXFP8 only): the bf16-first variant, which quantises the fp32
 // activation rounded to bf16 (the value the unfused chain stores and then
 // quantises) instead of the fp32 activation itself.  QUANT false: the
 // SiLU-and-mul of the unfused chain, which writes only the bf16 activation
 // (rounded as MODE's activation is) and no codes or scales.
-template <int MODE, int CPL, bool QBF16, bool QUANT>
+template <int MODE, int CPL, bool QBF16, bool QUANT, int ACT>
 __global__ void __launch_bounds__(256)
 act_quant_kernel(const ActArgs a)
 {
@@ -176,19 +263,19 @@ act_quant_kernel(const ActArgs a)
         if constexpr (!QUANT) {
             // the unfused SiLU-and-mul: the activation alone
             const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
-            float sg[8];
-            if constexpr (MODE == kMX) silu_f32x8(g, sg);
-            else silu_bf16x8(g, gv[k], sg);
+            if constexpr (MODE == kMX) {
+                act_f32xn<ACT, 8>(a, g, v);
+            } else {
+                float sg[8];
+                silu_bf16x8(g, gv[k], sg);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+                for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+            }
             stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
         } else if constexpr (MODE == kMX) {
             const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
             uint2 q;
-            float sg[8];
-            silu_f32x8(g, sg);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= sg[i];
+            act_f32xn<ACT, 8>(a, g, v);
             const uint4 ap = QBF16 ? round8<kBF16>(v) : pack8<kBF16>(v);
             if (a.act) stg_stream(a.act + out_off * 2, ap);
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
@@ -203,14 +290,97 @@ act_quant_kernel(const ActArgs a)
     }
 }
 
+// Decode-size form of the MXFP8 activation kernel (SiLU-and-mul or the
+// clamped SwiGLU; same arithmetic, same codes and scales) for quantising
+// launches without the bf16 copy: 4 activations per lane (8-byte loads of
+// gate and up), so a 32-element block spans 8 lanes (one half DPP row) and
+// a launch has twice the lanes.  At decode row counts the launch fills few
+// SIMDs, each wavefront runs alone, and the launch lasts about as long as
+// one wavefront's instruction chain; halving the work per lane shortens it.
+// a.C and a.dc describe 4-element chunks here.
+template <int ACT, bool QBF16>
+__global__ void __launch_bounds__(256)
+act_mx4_kernel(const ActArgs a)
+{
+    const uint32_t f = blockIdx.x * 256u + threadIdx.x;
+    // a row has I / 4 chunks, a multiple of 8, and blocks start at multiples
+    // of 256: every 8-lane block is either wholly inside the launch or
+    // wholly outside it
+    if (f >= a.total) return;
+    const uint32_t r = div_c(f, a.dc);
+    const int32_t lc = (int32_t)(f - r * (uint32_t)a.C);
+    const uint8_t *p = a.gu + (int64_t)r * a.gu_pitch + (int64_t)lc * 8;
+    const uint2 gv = ldg_stream8(p);
+    const uint2 uv = ldg_stream8(p + (int64_t)a.I * 2);
+    float g[4], v[4];
+    unpack4(gv, g);
+    unpack4(uv, v);
+    act_f32xn<ACT, 4>(a, g, v);
+    if constexpr (QBF16) {
+        const uint2 ap = pack4(v);
+        unpack4(ap, v); // quantise the bf16 activation
+    }
+    const uint32_t b = e8m0_of(max_oct(__builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                       __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])))));
+    const float ix = mx_inv_scale(b);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[0] * ix), clamp448(v[1] * ix), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[2] * ix), clamp448(v[3] * ix), w, true);
+    if ((lc & 7) == 0) a.scales[(int64_t)r * (a.I / 32) + lc / 8] = (uint8_t)b;
+    stg_stream(a.values + (int64_t)r * a.I + (int64_t)lc * 4, (uint32_t)w);
+}
+
 // ================================================================ launcher
-template <int MODE, int CPL, bool QBF16, bool QUANT = true>
+template <int MODE, int CPL, bool QBF16, bool QUANT = true, int ACT = kSilu>
 static hipError_t go_act(const ActArgs &a, hipStream_t st)
 {
     const uint32_t blocks = (a.total + 256u * CPL - 1) / (256u * CPL);
-    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL, QBF16, QUANT>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((act_quant_kernel<MODE, CPL, QBF16, QUANT, ACT>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
+
+// the 4-per-lane MXFP8 form (quantising launches without the bf16 copy):
+// a (total, C, dc) describe 8-element chunks on entry and are switched to
+// 4-element chunks here
+template <int ACT>
+static hipError_t go_act_mx4(ActArgs a, bool qbf16, hipStream_t st)
+{
+    a.total *= 2;
+    a.C *= 2;
+    a.dc = divc((uint32_t)a.C);
+    const uint32_t blocks = (a.total + 255u) / 256u;
+    if (qbf16)
+        hipLaunchKernelGGL((act_mx4_kernel<ACT, true>), dim3(blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((act_mx4_kernel<ACT, false>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// alpha log2(e) split into a 16-significant-bit head and the rest (times
+// ln 2), so that the head times a bf16 gate is exact in fp32
+static void swiglu_split(float alpha, float &hi, float &lo_ln2)
+{
+    const double c = (double)alpha * 1.4426950408889634;
+    int e = 0;
+    const double m = std::frexp(c, &e);
+    const double h = std::ldexp(std::nearbyint(std::ldexp(m, 16)), e - 16);
+    hi = (float)h;
+    lo_ln2 = (float)((c - h) * 0.6931471805599453);
+}
+
+// Quantising MXFP8 launches with no bf16 copy and at most this many
+// 8-element chunks take the 4-per-lane form (act_mx4_kernel).  Measured at
+// I = 768, hot, graph-replayed: the launch alone is faster from 64 to 1024
+// rows (clamped SwiGLU 1.95 -> 1.86 us at 64 rows, 1.98 -> 1.88 at 192,
+// 2.24 -> 2.12 at 1024; SiLU-and-mul 1.90 -> 1.82 at 192), the same within
+// noise at 8 rows, and slower from 2048 rows (196,608 chunks) on.  A kernel
+// that reads the codes right after it runs as fast as after the 8-per-lane
+// form; one that reads a bf16 activation written by the 4-per-lane form
+// (8-byte stores) ran 0.3-0.4 us slower, so copy-only launches and launches
+// that write the copy keep the 8-per-lane form.
+#ifndef AFQ_MX4_MAX_CHUNKS
+#define AFQ_MX4_MAX_CHUNKS 131072
+#endif
+constexpr int64_t kMx4MaxChunks = AFQ_MX4_MAX_CHUNKS;
 
 int launch_act(const ActPlan &p, void *stream)
 {
@@ -229,11 +399,24 @@ int launch_act(const ActPlan &p, void *stream)
         a.I = p.I;
         a.total = (uint32_t)(rows * C);
         a.dc = divc((uint32_t)C);
-        hipError_t e = !p.quant      ? (p.mode == kMX ? go_act<kMX, 1, false, false>(a, st)
-                                                     : go_act<kB128, 1, false, false>(a, st))
-                     : p.mode != kMX ? go_act<kB128, 1, false>(a, st)
-                     : p.qin == 2    ? go_act<kMX, 1, true>(a, st)
-                                     : go_act<kMX, 1, false>(a, st);
+        a.alpha = p.alpha;
+        a.beta = p.beta;
+        a.limit = p.limit;
+        swiglu_split(p.alpha, a.cHi, a.cLoLn2);
+        hipError_t e;
+        if (p.mode == kMX && p.quant && !p.act && (int64_t)a.total <= kMx4MaxChunks)
+            e = p.act_kind == kSwigluOai ? go_act_mx4<kSwigluOai>(a, p.qin == 2, st)
+                                         : go_act_mx4<kSilu>(a, p.qin == 2, st);
+        else if (p.act_kind == kSwigluOai) // MXFP8 only
+            e = !p.quant       ? go_act<kMX, 1, false, false, kSwigluOai>(a, st)
+                : p.qin == 2   ? go_act<kMX, 1, true, true, kSwigluOai>(a, st)
+                               : go_act<kMX, 1, false, true, kSwigluOai>(a, st);
+        else
+            e = !p.quant      ? (p.mode == kMX ? go_act<kMX, 1, false, false>(a, st)
+                                               : go_act<kB128, 1, false, false>(a, st))
+                : p.mode != kMX ? go_act<kB128, 1, false>(a, st)
+                : p.qin == 2    ? go_act<kMX, 1, true>(a, st)
+                                : go_act<kMX, 1, false>(a, st);
         if (e != hipSuccess) return (int)e;
     }
     return 0;

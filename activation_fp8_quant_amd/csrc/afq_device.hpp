@@ -140,6 +140,15 @@ __device__ __forceinline__ float max_quad(float f)
     v = max(v, dppu<kQuadSwap2>(v));
     return __uint_as_float(v);
 }
+// max over the 8 lanes of a half DPP row (an MXFP8 block at 4 values per
+// lane): after the quad step every lane holds its quad's max, and the
+// half-row mirror pairs each lane with one of the other quad
+__device__ __forceinline__ float max_oct(float f)
+{
+    uint32_t v = __float_as_uint(max_quad(f));
+    v = max(v, dppu<kRowHalfMirror>(v));
+    return __uint_as_float(v);
+}
 // max over the 16 lanes of a DPP row (a 1x128 group)
 __device__ __forceinline__ float max_row16(float f)
 {
@@ -407,6 +416,14 @@ __device__ __forceinline__ void stg_stream(void *p, const uint4 &v)
 __device__ __forceinline__ void stg_stream(void *p, const uint2 &v)
 {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2 *>(p));
+}
+__device__ __forceinline__ void stg_stream(void *p, uint32_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+}
+__device__ __forceinline__ uint2 ldg_stream8(const void *p)
+{
+    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p)));
 }
 
 } // namespace afq

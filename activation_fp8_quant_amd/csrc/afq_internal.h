@@ -42,6 +42,8 @@ struct ActPlan {
     int32_t mode;           // also the activation's rounding when copy only
     int32_t qin;            // 0 mode default, 2 bf16-rounded activation (MX)
     int32_t quant;          // 1 quantise; 0 copy only (values, scales nullptr)
+    int32_t act_kind;       // 0 SiLU-and-mul, 1 clamped SwiGLU (MX only)
+    float alpha, beta, limit; // clamped SwiGLU parameters
 };
 
 struct QuantPlan {

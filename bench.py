@@ -187,27 +187,36 @@ class NormCase:
 
 
 class SiluCase:
-    def __init__(self, M, I, *, seed, std, mode, sets=1, qin=0):
+    """SiLU-and-mul + quant, or with swiglu = (alpha, beta, limit) the
+    clamped SwiGLU + MXFP8."""
+
+    def __init__(self, M, I, *, seed, std, mode, sets=1, qin=0, swiglu=None):
         import torch
         import activation_fp8_quant_amd as afq
         from activation_fp8_quant_amd import inputs
         self.afq = afq
         self.mode = {"mx": afq.MXFP8, "b128": afq.BLOCK128}[mode]
+        self.swiglu = swiglu
+        self.qin = qin
         gu = _dev16(inputs.gate_up_inputs(M, I, seed=seed, std=std))
         self.sets = []
         for i in range(sets):
             gi = gu if i == 0 else gu.clone()
-            proto = afq.silu_mul_quant(gi, self.mode, quant_input=qin)
+            proto = self._launch(gi, None)
             self.sets.append((gi, (proto.values, proto.scales, None)))
-        self.qin = qin
         self.i = 0
         self.bytes = silu_bytes(M, I, mode=mode)
         torch.cuda.synchronize()
 
+    def _launch(self, g, out):
+        if self.swiglu:
+            return self.afq.swiglu_oai_quant(g, *self.swiglu, out=out, quant_input=self.qin)
+        return self.afq.silu_mul_quant(g, self.mode, out=out, quant_input=self.qin)
+
     def __call__(self):
         g, out = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
-        self.afq.silu_mul_quant(g, self.mode, out=out, quant_input=self.qin)
+        self._launch(g, out)
 
 
 class TwoSegCase:
@@ -278,29 +287,37 @@ class NormChainCase:
 
 class SiluChainCase:
     """The unfused SiLU chain on this library's kernels: a copy-only
-    SiLU-and-mul launch (bf16 activation), then the standalone quantiser."""
+    SiLU-and-mul launch (bf16 activation), then the standalone quantiser.
+    With swiglu = (alpha, beta, limit): the clamped SwiGLU's chain."""
 
-    def __init__(self, M, I, *, seed, std, mode, sets=1):
+    def __init__(self, M, I, *, seed, std, mode, sets=1, swiglu=None):
         import torch
         import activation_fp8_quant_amd as afq
         from activation_fp8_quant_amd import inputs
         self.afq = afq
         self.mode = {"mx": afq.MXFP8, "b128": afq.BLOCK128}[mode]
+        self.swiglu = swiglu
         gu = _dev16(inputs.gate_up_inputs(M, I, seed=seed, std=std))
         self.sets = []
         for i in range(sets):
             gi = gu if i == 0 else gu.clone()
-            plain = self.afq.silu_mul_quant(gi, self.mode, quantize=False)
+            plain = self._act(gi, None)
             q = afq.fp8_quant(plain.normed, self.mode)
             self.sets.append((gi, plain.normed, (q.values, q.scales, None)))
         self.i = 0
         self.bytes = M * (4 * I + 2 * I + 2 * I + I + I // 32)
         torch.cuda.synchronize()
 
+    def _act(self, g, act):
+        out = None if act is None else (None, None, act)
+        if self.swiglu:
+            return self.afq.swiglu_oai_quant(g, *self.swiglu, quantize=False, out=out)
+        return self.afq.silu_mul_quant(g, self.mode, quantize=False, out=out)
+
     def __call__(self):
         g, act, out = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
-        self.afq.silu_mul_quant(g, self.mode, quantize=False, out=(None, None, act))
+        self._act(g, act)
         self.afq.fp8_quant(act, self.mode, out=out)
 
 
@@ -427,6 +444,27 @@ def run_sweep():
                  M, M * (9 * 768 + 768 // 32), hot=True, page_us_swiglu_oai=PAGE_SWIGLU_CHAIN_US[M])
         ch["saved_us"] = round(ch["us_per_launch"] - fused_s["us_per_launch"], 2)
         ch["page_saved_us_swiglu_oai"] = PAGE_SWIGLU_SAVED_US[M]
+    # the clamped SwiGLU the pages time (swiglu_oai(gu, 1.702, 1.0, 7.0) on
+    # gu = randn * 8): fused, the unfused chain, what the fusion saves, and
+    # how many codes and scales the fp32 fusion changes against the chain
+    import activation_fp8_quant_amd as afq
+    oai = (1.702, 1.0, 7.0)
+    for M in DECODE_M:
+        fz = rec("f2", "clamped SwiGLU (swiglu_oai 1.702, 1.0, 7.0) + MXFP8, I=768, gate_up ~ N(0, 8^2)",
+                 lambda k, M=M: SiluCase(M, 768, seed=0, std=8.0, mode="mx", sets=k, swiglu=oai), M,
+                 silu_bytes(M, 768), hot=True, page_us=PAGE_SWIGLU_US[M], eager=True)
+        ch = rec("f2", "unfused chain: copy-only clamped SwiGLU, then MXFP8 quant (2 launches), I=768",
+                 lambda k, M=M: SiluChainCase(M, 768, seed=0, std=8.0, mode="mx", sets=k, swiglu=oai),
+                 M, M * (9 * 768 + 768 // 32), hot=True, page_us=PAGE_SWIGLU_CHAIN_US[M])
+        ch["saved_us"] = round(ch["us_per_launch"] - fz["us_per_launch"], 2)
+        ch["page_saved_us"] = PAGE_SWIGLU_SAVED_US[M]
+        from activation_fp8_quant_amd import inputs
+        g = _dev16(inputs.gate_up_inputs(M, 768, seed=0, std=8.0))
+        f = afq.swiglu_oai_quant(g, *oai)
+        q = afq.fp8_quant(afq.swiglu_oai_quant(g, *oai, quantize=False).normed, afq.MXFP8)
+        fz["codes_differ_vs_chain"] = round((f.values.view(torch.uint8) != q.values.view(torch.uint8))
+                                            .float().mean().item(), 4)
+        fz["scales_differ_vs_chain"] = round((f.scales != q.scales).float().mean().item(), 4)
     for M in (256, 1024):
         rec("C1", c1, norm_c1(M), M, norm_bytes(M, 6144))
     for M in (1, 32, 256, 4096):
@@ -446,7 +484,6 @@ def run_sweep():
         lambda k: NormCase(4096, 6144, seed=1, x_std=3.0, r_std=3.0, w_kind="normal", w_param=0.1,
                            kind="gemma", mode="mx", sets=k), 4096, norm_bytes(4096, 6144))
     # rounding-point variants: fp32-direct 1x128 norm, bf16-first MXFP8 SiLU
-    import activation_fp8_quant_amd as afq
     for M in (32, 4096):
         rec("f2", "add + standard RMSNorm + 1x128, fp32-direct (quantise the fp32 normed value), H=4096",
             lambda k, M=M: NormCase(M, 4096, seed=0, x_std=1.0, r_std=1.0, w_kind="uniform",
@@ -489,8 +526,10 @@ PROFILE_WORKLOADS = {
     "norm_mx_m8": lambda: NormCase(8, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal",
                                    w_param=0.1, kind="gemma", mode="mx"),
     "silu_mx_i768_m8": lambda: SiluCase(8, 768, seed=0, std=2.0, mode="mx"),
+    "swiglu_mx_i768_m8": lambda: SiluCase(8, 768, seed=0, std=8.0, mode="mx",
+                                          swiglu=(1.702, 1.0, 7.0)),
 }
-PROFILE_BY_GRAPH = {"norm_mx_m8", "silu_mx_i768_m8"}
+PROFILE_BY_GRAPH = {"norm_mx_m8", "silu_mx_i768_m8", "swiglu_mx_i768_m8"}
 
 
 def replay_launches(fn, launches, per_graph=200):

@@ -9,6 +9,7 @@
  *   fused_add_rmsnorm_quant  residual add + RMSNorm (Gemma or standard),
  *                            one or two row segments per launch
  *   silu_mul_quant           SiLU-and-mul on a [gate | up] row
+ *   swiglu_oai_quant         the clamped SwiGLU on a [gate | up] row
  *   fp8_quant                the standalone row-wise quantiser (the
  *                            "separate quant" the fused kernels replace)
  *
@@ -67,6 +68,17 @@
  *             SiLU-and-mul -> quant chain stores it (vLLM pull request
  *             65478, "Test Plan / Correctness").
  *
+ * Clamped SwiGLU (swiglu_oai_quant; MXFP8 only), per element j of a row:
+ *   gc_j = min(gate_j, limit),  uc_j = min(max(up_j, -limit), limit)
+ *   a_j  = fp32(fp32(gc_j * logistic(alpha * gc_j)) * fp32(uc_j + beta))
+ *   quantised like the MXFP8 SiLU-and-mul (quant_input AFQ_QIN_BF16: a_j
+ *   rounded to bf16 first).  vLLM pull request 65478 ("Microbenchmark
+ *   script") times this activation as swiglu_oai(gu, 1.702, 1.0, 7.0) with a
+ *   fused fp32 swiglu + MXFP8 kernel ("Purpose", commit 2); the pages do not
+ *   write the function out, and the form above is the clamped SwiGLU
+ *   published with OpenAI's gpt-oss models.  The kernel's fp32 gate factor
+ *   is within a few ulp of fp32(gc * logistic(alpha * gc)).
+ *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless stated otherwise; descriptors are
  *     host memory read during the call only.
@@ -117,7 +129,7 @@
 extern "C" {
 #endif
 
-#define AFQ_ABI_VERSION 3
+#define AFQ_ABI_VERSION 4
 
 /* Return codes. */
 enum {
@@ -247,6 +259,24 @@ typedef struct afq_act_desc {
 } afq_act_desc;
 
 /*
+ * swiglu_oai_quant descriptor (ABI 4).
+ *   act     rows, width, input, quant_input and outputs exactly as for
+ *           silu_mul_quant; act.mode must be AFQ_MXFP8 (otherwise
+ *           AFQ_ERR_UNSUPPORTED).  A copy-only launch (values and scales
+ *           NULL) writes the bf16 activation bf16(a_j).
+ *   alpha   slope of the logistic gate; finite
+ *   beta    added to the clamped up value; finite
+ *   limit   clamp bound; > 0, +inf allowed (no clamping)
+ * Bad alpha, beta or limit: AFQ_ERR_ARG.
+ */
+typedef struct afq_swiglu_desc {
+    afq_act_desc act;
+    float alpha;
+    float beta;
+    float limit;
+} afq_swiglu_desc;
+
+/*
  * fp8_quant descriptor: the standalone quantiser of an activation that is
  * already in HBM (the "separate quant" of the unfused chains: vLLM pull
  * request 65478 mxfp8_e4m3_quantize, "Kernel-level measurements"; SGLang
@@ -271,6 +301,9 @@ int fused_add_rmsnorm_quant(const afq_norm_desc *desc, void *stream);
 
 /* SiLU-and-mul + quantisation.  Returns AFQ_OK or an AFQ_ERR_*. */
 int silu_mul_quant(const afq_act_desc *desc, void *stream);
+
+/* Clamped SwiGLU + MXFP8 quantisation.  Returns AFQ_OK or an AFQ_ERR_*. */
+int swiglu_oai_quant(const afq_swiglu_desc *desc, void *stream);
 
 /* Standalone row-wise quantisation.  Returns AFQ_OK or an AFQ_ERR_*. */
 int fp8_quant(const afq_quant_desc *desc, void *stream);

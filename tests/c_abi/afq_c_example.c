@@ -5,9 +5,10 @@
  * include/afq.h on seeded inputs, copies the outputs back and checks them
  * against the CPU oracle (oracle/afq_oracle.c, linked into this test
  * program): the fused add + Gemma RMSNorm + MXFP8 + copy, the 1x128
- * SiLU-and-mul and the standalone per-token quantiser; and that the unfused
- * chain (a copy-only norm launch, then fp8_quant) reproduces the fused
- * launch bit for bit.  Also checks the version and an error path.  Prints one line per check; exits non-zero on
+ * SiLU-and-mul, the clamped SwiGLU + MXFP8 and the standalone per-token
+ * quantiser; and that the unfused chain (a copy-only norm launch, then
+ * fp8_quant) reproduces the fused launch bit for bit.  Also checks the
+ * version and an error path.  Prints one line per check; exits non-zero on
  * the first failure.
  */
 #include "afq.h"
@@ -28,6 +29,10 @@ int orc_norm_quant_rows(int64_t M, int64_t H, const void *x, int64_t x_stride,
 int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
                         int mode, int qin, uint8_t *values, void *scales, uint16_t *act_out,
                         int64_t r0, int64_t r1, double *work);
+int orc_swiglu_oai_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
+                              int mode, int qin, float alpha, float beta, float limit,
+                              uint8_t *values, void *scales, uint16_t *act_out,
+                              int64_t r0, int64_t r1, double *work);
 int orc_quant_rows(int64_t M, int64_t n, const void *x, int64_t x_stride, int in_dtype,
                    int mode, uint8_t *values, void *scales, int64_t r0, int64_t r1, double *work);
 
@@ -183,6 +188,36 @@ int main(void)
         if (memcmp(gq, oq, M * I) != 0) FAIL("silu 1x128 codes not bit-identical");
         if (memcmp(gs, os, 4 * M * (I / 128)) != 0) FAIL("silu 1x128 scales not bit-identical");
         printf("silu 1x128 codes and scales: bit-identical (%lld elements)\n", (long long)(M * I));
+        CHECK_HIP(hipFree(dg)); CHECK_HIP(hipFree(dq)); CHECK_HIP(hipFree(ds)); CHECK_HIP(hipFree(da));
+        free(gu); free(gq); free(oq); free(gs); free(os); free(ga); free(oa);
+    }
+
+    /* ---- clamped SwiGLU (alpha 1.702, beta 1, limit 7) + MXFP8, M = 24, I = 768,
+     *      gate_up ~ N(0, 8^2) */
+    {
+        const int64_t M = 24, I = 768;
+        uint16_t *gu = malloc(4 * M * I);
+        for (int64_t i = 0; i < 2 * M * I; ++i) gu[i] = to_bf16((float)(8.0 * normal()));
+        void *dg = dmalloc(4 * M * I), *dq = dmalloc(M * I), *ds = dmalloc(M * (I / 32)), *da = dmalloc(2 * M * I);
+        up(dg, gu, 4 * M * I);
+        afq_swiglu_desc d;
+        memset(&d, 0, sizeof d);
+        d.act.M = M; d.act.I = I; d.act.gate_up = dg; d.act.gate_up_row_stride = 2 * I;
+        d.act.mode = AFQ_MXFP8; d.act.quant_input = AFQ_QIN_DEFAULT;
+        d.act.out.values = dq; d.act.out.scales = ds; d.act.out.normed = da;
+        d.alpha = 1.702f; d.beta = 1.0f; d.limit = 7.0f;
+        int stt = swiglu_oai_quant(&d, st);
+        if (stt != AFQ_OK) FAIL("swiglu_oai_quant: %s", afq_status_string(stt));
+        d.limit = 0.0f;
+        if (swiglu_oai_quant(&d, st) != AFQ_ERR_ARG) FAIL("limit 0 not rejected");
+        CHECK_HIP(hipStreamSynchronize(st));
+        uint8_t *gq = malloc(M * I), *oq = malloc(M * I), *gs = malloc(M * (I / 32)), *os = malloc(M * (I / 32));
+        uint16_t *ga = malloc(2 * M * I), *oa = malloc(2 * M * I);
+        down(gq, dq, M * I); down(gs, ds, M * (I / 32)); down(ga, da, 2 * M * I);
+        orc_swiglu_oai_quant_rows(M, I, gu, 2 * I, 0, 0, 1.702f, 1.0f, 7.0f, oq, os, oa, 0, M, work);
+        compare16("swiglu MXFP8 bf16 activation", ga, oa, M * I, 0);
+        compare_codes("swiglu MXFP8 codes", gq, oq, M * I);
+        compare_bytes("swiglu E8M0 scales", gs, os, M * (I / 32), 1);
         CHECK_HIP(hipFree(dg)); CHECK_HIP(hipFree(dq)); CHECK_HIP(hipFree(ds)); CHECK_HIP(hipFree(da));
         free(gu); free(gq); free(oq); free(gs); free(os); free(ga); free(oa);
     }

@@ -23,8 +23,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert {"fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant", "afq_status_string",
-            "afq_abi_version", "afq_last_hip_error"} <= set(names)
+    assert {"fused_add_rmsnorm_quant", "silu_mul_quant", "swiglu_oai_quant", "fp8_quant",
+            "afq_status_string", "afq_abi_version", "afq_last_hip_error"} <= set(names)
     out = subprocess.check_output(["nm", "-D", "--defined-only", afq.library_path], text=True)
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in names if n not in exported]
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert afq.abi_version() == 3
+    assert afq.abi_version() == 4
     for st in range(0, -9, -1):
         s = afq.status_string(st)
         assert s and s != "unknown status"
@@ -53,6 +53,7 @@ def test_descriptor_layout_matches_header(tmp_path):
                           "residual_out", "seg"],
         "afq_act_desc": ["M", "I", "gate_up", "gate_up_row_stride", "mode", "quant_input", "out"],
         "afq_quant_desc": ["M", "cols", "x", "x_row_stride", "dtype", "mode", "out"],
+        "afq_swiglu_desc": ["act", "alpha", "beta", "limit"],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "afq.h"', "int main(void){"]
     for st, fs in fields.items():
@@ -68,7 +69,8 @@ def test_descriptor_layout_matches_header(tmp_path):
         parts = line.split()
         c[tuple(parts[:-1])] = int(parts[-1])
     py = {"afq_qact": afq._QAct, "afq_norm_seg": afq._NormSeg, "afq_norm_desc": afq._NormDesc,
-          "afq_act_desc": afq._ActDesc, "afq_quant_desc": afq._QuantDesc}
+          "afq_act_desc": afq._ActDesc, "afq_quant_desc": afq._QuantDesc,
+          "afq_swiglu_desc": afq._SwigluDesc}
     for st, cls in py.items():
         assert c[(st, "size")] == ctypes.sizeof(cls), st
         for f in fields[st]:
@@ -238,6 +240,58 @@ def test_copy_only_validation():
     a.out.values = None
     a.mode = afq.PER_TOKEN
     assert lib.silu_mul_quant(ctypes.byref(a), None) == -6     # no per-token activation
+
+
+def test_swiglu_validation_errors():
+    """The clamped SwiGLU entry: MXFP8 only; alpha and beta finite, limit
+    positive (infinity allowed); the activation descriptor is checked as
+    silu_mul_quant checks it."""
+    lib = afq.load()
+    inf, nan = float("inf"), float("nan")
+
+    def desc(**kw):
+        d = afq._SwigluDesc()
+        a = d.act
+        a.M, a.I, a.gate_up, a.gate_up_row_stride, a.mode = 0, 768, A16, 1536, afq.MXFP8
+        a.out.values, a.out.scales = A16 * 64, A16 * 128
+        d.alpha, d.beta, d.limit = 1.702, 1.0, 7.0
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+
+    def call(d):
+        return lib.swiglu_oai_quant(ctypes.byref(d), None)
+
+    assert lib.swiglu_oai_quant(None, None) == -1
+    assert call(desc()) == 0                                   # M = 0: nothing enqueued
+    assert call(desc(limit=inf)) == 0
+    for bad in (dict(alpha=inf), dict(alpha=nan), dict(beta=-inf), dict(beta=nan),
+                dict(limit=0.0), dict(limit=-1.0), dict(limit=nan), dict(limit=-inf)):
+        assert call(desc(**bad)) == -7, bad
+    d = desc()
+    d.act.mode = afq.BLOCK128
+    assert call(d) == -6
+    d.act.mode = afq.PER_TOKEN
+    assert call(d) == -6
+    d.act.mode = 7
+    assert call(d) == -7
+    d = desc()
+    d.act.quant_input = afq.QIN_FP32
+    assert call(d) == -6
+    d.act.quant_input = afq.QIN_BF16
+    assert call(d) == 0
+    d = desc()
+    d.act.M, d.act.I = 4, 100
+    assert call(d) == -2                                       # no 1x32 width
+    d.act.I, d.act.gate_up_row_stride = 768, 1540
+    assert call(d) == -3
+    d.act.gate_up_row_stride = 1536
+    d.act.out.scales = None
+    assert call(d) == -1
+    d.act.out.values = None                                    # copy-only needs its copy
+    assert call(d) == -1
+    d.act.out.normed = A16 + 64                                # copy over the input
+    assert call(d) == -5
 
 
 def test_binding_refuses_without_library(monkeypatch):
