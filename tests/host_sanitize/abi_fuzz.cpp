@@ -76,6 +76,12 @@ int launch_act(const ActPlan &p, void *)
         require(!p.values && !p.scales && al(p.act, 16), "act: copy-only pointers");
     require(p.act == nullptr || al(p.act, 16), "act: copy pointer");
     require(p.gu_pitch >= (int64_t)p.I * 4 && p.gu_pitch % 16 == 0, "act: pitch");
+    require(p.act_kind == 0 || p.act_kind == 1, "act: activation kind");
+    if (p.act_kind == 1)
+        require(p.mode == AFQ_MXFP8 && std::isfinite(p.alpha) && std::isfinite(p.beta) &&
+                    p.limit > 0.0f && !std::isnan(p.limit), "act: clamped SwiGLU: MXFP8 and parameters");
+    else
+        require(p.alpha == 1.0f && p.beta == 0.0f && std::isinf(p.limit), "act: SiLU parameters");
     return 0;
 }
 int launch_quant(const QuantPlan &p, void *)
@@ -100,6 +106,8 @@ const int64_t kRows[] = {-5, -1, 0, 1, 2, 7, 64, 1025, 16384, AFQ_MAX_ROWS, (int
                          kBig, std::numeric_limits<int64_t>::min()};
 const int64_t kCols[] = {-8, 0, 7, 8, 16, 24, 32, 48, 128, 256, 512, 1536, 2176, 6144, 32768, 32776, kBig};
 const int32_t kEnum[] = {-1, 0, 1, 2, 3, 7};
+const float kPar[] = {1.702f, 1.0f, 7.0f, 0.0f, -0.5f, 1e-30f, 3e38f, std::numeric_limits<float>::infinity(),
+                      -std::numeric_limits<float>::infinity(), std::numeric_limits<float>::quiet_NaN()};
 const float kEps[] = {1e-6f, 0.0f, -1e-6f, 1e30f, std::numeric_limits<float>::infinity(),
                       std::numeric_limits<float>::quiet_NaN()};
 
@@ -135,11 +143,11 @@ bool documented(int st) { return st <= 0 && st >= -8; }
 
 int main()
 {
-    long counts[3][9] = {};
+    long counts[4][9] = {};
     const int iters = 200000;
     for (int it = 0; it < iters; ++it) {
         int st, st2;
-        switch (it % 3) {
+        switch (it % 4) {
         case 0: {
             afq_norm_desc d{};
             d.M = pick(kRows);
@@ -182,6 +190,25 @@ int main()
             st2 = silu_mul_quant(&d, nullptr);
             break;
         }
+        case 3: {
+            afq_swiglu_desc sd{};
+            afq_act_desc &d = sd.act;
+            d.M = pick(kRows);
+            d.I = pick(kCols);
+            d.gate_up_row_stride = stride_for(2 * (d.I > 0 && d.I < kBig / 4 ? d.I : 8));
+            d.gate_up = addr(0);
+            d.mode = rng() % 4 ? AFQ_MXFP8 : venum(3);
+            d.quant_input = rng() % 2 ? 0 : venum(3);
+            d.out.values = rng() % 8 ? addr(1) : nullptr;
+            d.out.scales = d.out.values ? addr(2) : nullptr;
+            d.out.normed = rng() % 2 ? addr(3) : nullptr;
+            sd.alpha = rng() % 3 ? 1.702f : pick(kPar);
+            sd.beta = rng() % 3 ? 1.0f : pick(kPar);
+            sd.limit = rng() % 3 ? 7.0f : pick(kPar);
+            st = swiglu_oai_quant(&sd, nullptr);
+            st2 = swiglu_oai_quant(&sd, nullptr);
+            break;
+        }
         default: {
             afq_quant_desc d{};
             d.M = pick(kRows);
@@ -202,15 +229,15 @@ int main()
         require(st != AFQ_ERR_LAUNCH, "no launch error from the stubs");
         require(st == st2, "same descriptor, same status");
         require(afq_status_string(st) != nullptr, "status string");
-        counts[it % 3][-st]++;
+        counts[it % 4][-st]++;
     }
-    const char *names[3] = {"fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant"};
-    for (int e = 0; e < 3; ++e) {
+    const char *names[4] = {"fused_add_rmsnorm_quant", "silu_mul_quant", "fp8_quant", "swiglu_oai_quant"};
+    for (int e = 0; e < 4; ++e) {
         std::printf("%s:", names[e]);
         for (int c = 0; c < 9; ++c) std::printf(" %d:%ld", -c, counts[e][c]);
         std::printf("\n");
     }
-    for (int e = 0; e < 3; ++e)
+    for (int e = 0; e < 4; ++e)
         require(counts[e][0] > 0, "some calls are accepted");
     return 0;
 }

@@ -21,6 +21,10 @@ int orc_norm_quant_rows(int64_t M, int64_t H, const void *x, int64_t x_stride,
 int orc_silu_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
                         int mode, int qin, uint8_t *values, void *scales, uint16_t *act_out,
                         int64_t r0, int64_t r1, double *work);
+int orc_swiglu_oai_quant_rows(int64_t M, int64_t I, const uint16_t *gu, int64_t gu_stride,
+                              int mode, int qin, float alpha, float beta, float limit,
+                              uint8_t *values, void *scales, uint16_t *act_out,
+                              int64_t r0, int64_t r1, double *work);
 uint16_t orc_round_bf16(double v);
 uint16_t orc_round_fp16(double v);
 uint8_t orc_round_e4m3(double v);
@@ -107,6 +111,17 @@ int main(void)
                 rows_done += M;
             }
         if (orc_silu_quant_rows(M, H, gu, 2 * H, 2, 0, q, sc, nrm, 0, M, work) != -1) return 1; /* per-token */
+        if (H % 32 == 0) {
+            const float par[3][3] = {{1.702f, 1.0f, 7.0f}, {1.0f, 0.0f, INFINITY}, {-0.5f, -3.0f, 1e-3f}};
+            for (int k = 0; k < 3; ++k)
+                for (int qin = 0; qin < 3; qin += 2) {
+                    if (orc_swiglu_oai_quant_rows(M, H, gu, 2 * H, 0, qin, par[k][0], par[k][1], par[k][2],
+                                                  q, sc, nrm, 0, M, work) != 0) return 1;
+                    rows_done += M;
+                }
+        }
+        if (orc_swiglu_oai_quant_rows(M, H, gu, 2 * H, 1, 0, 1.702f, 1.0f, 7.0f, q, sc, nrm, 0, M, work) != -1)
+            return 1; /* MXFP8 only */
         free(x); free(r); free(wt); free(h); free(nrm); free(gu); free(q); free(sc); free(xf);
     }
     /* the scalar format helpers at their boundaries */

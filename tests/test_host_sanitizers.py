@@ -36,7 +36,7 @@ def test_abi_validation_fuzz(tmp_path):
     r = _run([exe], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
     assert r.returncode == 0, r.stdout + r.stderr
     assert "runtime error" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr
-    assert r.stdout.count(" 0:") == 3, r.stdout
+    assert r.stdout.count(" 0:") == 4, r.stdout
 
 
 def test_oracle_paths(tmp_path):
