@@ -276,6 +276,36 @@ __device__ __forceinline__ double lds_rows_sum_f64(const double *p0, const doubl
     return join64(__builtin_amdgcn_readlane(lo, 0), __builtin_amdgcn_readlane(hi, 0));
 }
 
+// Sum of a row's block totals, p0[0..nb) and p1[0..nb) for a second
+// segment (one total per 64-chunk block of the row, nb <= 64), in a tree
+// fixed by nb, a function of the row width alone: up to 16 blocks the
+// 16-lane tree of lds_rows_sum (both segments in one pass), more blocks the
+// 64-lane wavefront tree per segment.  Lanes past nb add zeros, which add
+// exactly (the totals are sums of squares, never -0).
+template <int NSEG>
+__device__ __forceinline__ float lds_blocks_sum(const float *p0, const float *p1, int nb, float &t1)
+{
+    if (nb <= 16) return lds_rows_sum<NSEG>(p0, p1, nb, t1);
+    const int l = threadIdx.x & 63;
+    const float t0 = lane_pick(sum_wave(l < nb ? p0[l] : 0.f), 0);
+    t1 = NSEG > 1 ? lane_pick(sum_wave(l < nb ? p1[l] : 0.f), 0) : 0.f;
+    return t0;
+}
+__device__ __forceinline__ double lane_pick_f64(double v, int lane)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    return join64(__builtin_amdgcn_readlane((uint32_t)b, lane), __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane));
+}
+template <int NSEG>
+__device__ __forceinline__ double lds_blocks_sum_f64(const double *p0, const double *p1, int nb, double &t1)
+{
+    if (nb <= 16) return lds_rows_sum_f64<NSEG>(p0, p1, nb, t1);
+    const int l = threadIdx.x & 63;
+    const double t0 = lane_pick_f64(sum_wave_f64(l < nb ? p0[l] : 0.0), 0);
+    t1 = NSEG > 1 ? lane_pick_f64(sum_wave_f64(l < nb ? p1[l] : 0.0), 0) : 0.0;
+    return t0;
+}
+
 // Block barrier that orders only LDS: the waves exchange reduction
 // partials through LDS, and their outstanding global stores need not
 // complete before the barrier (a __syncthreads() would wait for them).

@@ -31,31 +31,90 @@ __device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
     return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
 }
 
-// Row shape for a row of C chunks: one chunk per lane (as many lanes as
-// chunks, up to 1024), so that a row's loads are all in flight at once and
-// the per-lane work is shortest.  Per-token rows of a bandwidth-bound
-// launch (M > 1024) take two chunks per lane instead: they need two row
-// reductions (sum of squares, then amax), each an LDS exchange across the
-// row's wavefronts, and halving the wavefronts per row pays for the longer
-// lane work (measured at M = 8192, H = 2048..8192: per-token 4-14% faster
-// at two chunks; MXFP8 1-3% and 1x128 within 1% faster at one).  NT is a
-// whole number of wavefronts; rows of fewer than 256 lanes are packed
-// several to a block.
+// Row shapes of the row kernels.  A row of C chunks runs on NT lanes (a
+// whole number of wavefronts, at most 1024), CPL = ceil(C / NT) chunks per
+// lane; rows of fewer than 256 lanes are packed several to a block.
 struct RowShapeRt {
     int NT, CPL, R, WPR;
 };
-static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
+static inline int row_lanes(int C, int cpl)
 {
-    RowShapeRt s;
-    int cpl = (per_token && M > 1024) ? 2 : 1;
+    const int nt = (C + cpl - 1) / cpl;
+    return (nt + 63) / 64 * 64;
+}
+static inline RowShapeRt shape_at(int C, int cpl)
+{
     if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
-    int nt = (C + cpl - 1) / cpl;
-    nt = (nt + 63) / 64 * 64;
+    RowShapeRt s;
+    const int nt = row_lanes(C, cpl);
     s.NT = nt;
     s.CPL = (C + nt - 1) / nt;
     s.R = (nt < 256 && 256 % nt == 0) ? 256 / nt : 1;
     s.WPR = nt / 64;
     return s;
+}
+
+// The standalone per-token quantiser: one chunk per lane (as many lanes as
+// chunks, up to 1024), so that a row's loads are all in flight at once and
+// the per-lane work is shortest, except in launches above 1024 rows, which
+// take two chunks per lane.
+static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
+{
+    return shape_at(C, (per_token && M > 1024) ? 2 : 1);
+}
+
+// Rows of the norm kernel that one round of the GPU holds at cpl chunks per
+// lane: 256 CUs, each with 32 wavefront slots (8 per SIMD; 7 at four chunks
+// per lane, where the kernel needs more than 64 VGPRs), whole rows per CU.
+constexpr int64_t kCUs = 256;
+static inline int64_t norm_rows_per_round(int C, int cpl)
+{
+    const int waves = row_lanes(C, cpl) / 64;
+    const int slots = cpl >= 4 ? 28 : 32;
+    return kCUs * (slots / waves);
+}
+
+// The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
+// 2048 / 4096 / 6144 / 8192, 1 to 4096 rows, one to four chunks per lane):
+//  * per-token (two row reductions, each an LDS exchange across the row's
+//    wavefronts): up to 256 rows, rows of 256 to 512 lanes (two chunks per
+//    lane for rows wider than 2048; 7-23 % faster at widths 4096-8192, 8
+//    rows); above 256 rows, the fewest chunks per lane from two up whose
+//    row is a whole divisor of a CU's 32 wavefront slots (13-44 % faster
+//    than one chunk per lane from 512 rows: at width 6144, 4096 rows,
+//    27.6 -> 15.4 us at three chunks per lane);
+//  * MXFP8 with the copy: when one chunk per lane needs two or three rounds
+//    of rows, the fewest chunks per lane that hold every row in one round
+//    (7-13 % faster: width 6144, 1024 rows 12.8 -> 11.3 us; width 4096,
+//    3072 rows 21.7 -> 20.2 us at four chunks per lane); one chunk per lane
+//    otherwise (at one round it is as fast, at four or more rounds the
+//    launch is bandwidth-bound and longer lane work only costs);
+//  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
+//    per lane, which the same sweep found best for 1x128 at every size.
+static inline RowShapeRt norm_row_shape(int C, int64_t M, int mode, bool copy)
+{
+    int cpl = 1;
+    if (mode == kPT) {
+        if (M <= 256) {
+            cpl = C > 256 ? 2 : 1;
+        } else {
+            cpl = 2;
+            for (int c = 2; c <= 4; ++c)
+                if (32 % (row_lanes(C, c) / 64) == 0) {
+                    cpl = c;
+                    break;
+                }
+        }
+    } else if (mode == kMX && copy) {
+        const int64_t r1 = norm_rows_per_round(C, 1);
+        if (M > r1 && M <= 3 * r1)
+            for (int c = 2; c <= 4; ++c)
+                if (norm_rows_per_round(C, c) >= M) {
+                    cpl = c;
+                    break;
+                }
+    }
+    return shape_at(C, cpl);
 }
 
 // Rows per launch of the flat kernels: the flat chunk index stays below

@@ -55,6 +55,21 @@ __device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
     return acc;
 }
 
+// The sum of squares is formed in an order fixed by the row width alone, so
+// that a row's outputs do not depend on the launch's row shape (and through
+// it on the row count): each chunk's 8 squares in a fixed chain, each
+// aligned 64-chunk block of the row by the wavefront tree, the blocks by a
+// tree over their index (lds_blocks_sum).  At one chunk per lane every
+// wavefront of the row is one block, and the first program below forms
+// that order directly (lanes past the row skip their loads and stores); at
+// two to four chunks per lane the second reduces each of a wavefront's
+// slots (one block each) separately and adds the blocks in LDS.  In the
+// second, lanes off the row load the first chunk of the last row and
+// compute like every lane, only their stores are skipped: no branch skips
+// a load or its use, which keeps the compiler's waits on the vector memory
+// counter exact (with a load it had to assume pending, it waited for every
+// store in flight too).
+//
 // F32Q (1x128 / per-token): the fp32-direct variant.  The quantiser reads
 // the fp32 normed value y = fl32(fl32(h * inv32) * g32) instead of its
 // dtype rounding, with inv32 = fl32(1 / sqrt(mean(h^2) + eps)).  To make
@@ -72,201 +87,446 @@ template <int DT, int MODE, bool GEMMA, int CPL, int NSEG, bool SEGU, bool F32Q>
 __global__ void __launch_bounds__(kMaxBlock)
 norm_quant_kernel(const NormArgs a)
 {
-    const int tid = threadIdx.x;
-    // rows are whole wavefronts: the wavefront, its row and everything
-    // derived from them are wavefront-uniform (kept in scalar registers)
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
-    const int t = tid - rib * a.NT;                       // lane within the row
-    const int tw = wave * 64 - rib * a.NT;                // t of the wavefront's lane 0
-    const int64_t row = (int64_t)blockIdx.x * a.R + rib;
-    const bool row_ok = row < a.M;
-    const bool has_res = a.res_in != nullptr;
+    if constexpr (CPL == 1) {
+        const int tid = threadIdx.x;
+        // rows are whole wavefronts: the wavefront, its row and everything
+        // derived from them are wavefront-uniform (kept in scalar registers)
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
+        const int t = tid - rib * a.NT;                       // lane within the row
+        const int tw = wave * 64 - rib * a.NT;                // t of the wavefront's lane 0
+        const int64_t row = (int64_t)blockIdx.x * a.R + rib;
+        const bool row_ok = row < a.M;
+        const bool has_res = a.res_in != nullptr;
 
-    // per-row bases
-    const uint8_t *xrow0 = a.seg[0].x + row * a.seg[0].x_pitch;
-    const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + row * a.seg[1].x_pitch : xrow0;
-    const int64_t rrow = row * a.C0 * 16;
+        // per-row bases
+        const uint8_t *xrow0 = a.seg[0].x + row * a.seg[0].x_pitch;
+        const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + row * a.seg[1].x_pitch : xrow0;
+        const int64_t rrow = row * a.C0 * 16;
 
-    // ---- issue every load of the row
-    uint4 xv[CPL], rv[CPL], wv[CPL];
-    bool ok[CPL];
-    int sg[CPL], lc[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const int c = t + k * a.NT;
-        ok[k] = row_ok && c < a.C;
-        if constexpr (NSEG == 1) {
-            sg[k] = 0;
-            lc[k] = c;
-        } else {
-            sg[k] = (SEGU ? tw + k * a.NT : c) >= a.C0 ? 1 : 0;
-            lc[k] = c - (sg[k] ? a.C0 : 0);
-        }
-        if (ok[k]) {
-            xv[k] = ldg_stream((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
-            wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
-            if (has_res)
-                rv[k] = ldg_stream(a.res_in + rrow + lc[k] * 16);
-        }
-    }
-
-    // ---- residual add (h = round_dt(x + r), stored), sum of squares
-    float h[CPL][8];
-    float ss0 = 0.f, ss1 = 0.f;
-    double sd0 = 0.0, sd1 = 0.0; // F32Q
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        if (!ok[k]) continue;
-        uint4 hp = xv[k];
-        if (has_res) {
-            float rf[8];
-            unpack8<DT>(xv[k], h[k]);
-            unpack8<DT>(rv[k], rf);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
-            hp = pack8<DT>(h[k]);
-            stg_stream(a.res_out + rrow + lc[k] * 16, hp);
-        }
-        unpack8<DT>(hp, h[k]);
-        if constexpr (F32Q) {
-            double sd = 0.0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sd = __builtin_fma((double)h[k][i], (double)h[k][i], sd);
-            if (NSEG > 1 && sg[k]) sd1 += sd;
-            else sd0 += sd;
-        } else {
-            if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
-            else ss0 = sumsq8<DT>(hp, ss0);
-        }
-    }
-
-    // segments this wavefront holds chunks of (with SEGU a scalar fact; a
-    // segment it does not hold contributes zeros, so its reduction is skipped)
-    bool has0 = true, has1 = NSEG > 1;
-    if constexpr (NSEG > 1 && SEGU) {
-        has0 = false;
-        has1 = false;
-#pragma unroll
+        // ---- issue every load of the row
+        uint4 xv[CPL], rv[CPL], wv[CPL];
+        bool ok[CPL];
+        int sg[CPL], lc[CPL];
+    #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-            if (sg[k]) has1 = true;
-            else has0 = true;
+            const int c = t + k * a.NT;
+            ok[k] = row_ok && c < a.C;
+            if constexpr (NSEG == 1) {
+                sg[k] = 0;
+                lc[k] = c;
+            } else {
+                sg[k] = (SEGU ? tw + k * a.NT : c) >= a.C0 ? 1 : 0;
+                lc[k] = c - (sg[k] ? a.C0 : 0);
+            }
+            if (ok[k]) {
+                xv[k] = ldg_stream((sg[k] ? xrow1 : xrow0) + lc[k] * 16);
+                wv[k] = ldg<uint4>((sg[k] ? a.seg[1].w : a.seg[0].w) + lc[k] * 16);
+                if (has_res)
+                    rv[k] = ldg_stream(a.res_in + rrow + lc[k] * 16);
+            }
         }
-    }
 
-    // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
-    //      across the wavefronts of the row
-    // (LDS partials are segment-major: a row's partials are contiguous)
-    const int p0 = rib * a.WPR;
-    __shared__ float redm[2][kMaxBlock / 64];
-    float inv0, inv1;
-    if constexpr (F32Q) {
-        __shared__ double redd[2][kMaxBlock / 64];
-        if (has0) sd0 = sum_wave_f64(sd0);
-        if constexpr (NSEG > 1)
-            if (has1) sd1 = sum_wave_f64(sd1);
-        if (a.WPR > 1) {
-            if ((tid & 63) == 0) {
-                redd[0][wave] = sd0;
-                if constexpr (NSEG > 1) redd[1][wave] = sd1;
-            }
-            lds_barrier();
-            sd0 = lds_rows_sum_f64<NSEG>(&redd[0][p0], &redd[1][p0], a.WPR, sd1);
-        }
-        inv0 = (float)(1.0 / sqrt(sd0 / (double)a.seg[0].cols + (double)a.eps));
-        inv1 = NSEG > 1 ? (float)(1.0 / sqrt(sd1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
-    } else {
-        __shared__ float red[2][kMaxBlock / 64];
-        if (has0) ss0 = sum_wave(ss0);
-        if constexpr (NSEG > 1)
-            if (has1) ss1 = sum_wave(ss1);
-        if (a.WPR > 1) {
-            if ((tid & 63) == 0) {
-                red[0][wave] = ss0;
-                if constexpr (NSEG > 1) red[1][wave] = ss1;
-            }
-            lds_barrier();
-            ss0 = lds_rows_sum<NSEG>(&red[0][p0], &red[1][p0], a.WPR, ss1);
-        }
-        inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
-        inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
-    }
-
-    // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
-    //      Gemma: g * inv = (1 + w) inv as one FMA.  F32Q: y = (h inv) g
-    //      in that order is kept in place of h (the quantiser's input), and
-    //      only the copy is rounded.
-    float am0 = 0.f, am1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        if (!ok[k]) continue;
-        const float inv = sg[k] ? inv1 : inv0;
-        float wf[8];
-        unpack8<DT>(wv[k], wf);
-        if constexpr (F32Q) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float g = GEMMA ? 1.0f + wf[i] : wf[i];
-                h[k][i] = (h[k][i] * inv) * g;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
-        }
-        const uint4 up = F32Q ? pack8<DT>(h[k]) : round8<DT>(h[k]);
-        uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
-        const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
-        if (normed)
-            stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
-        if constexpr (MODE == kPT) {
-            const float m = amax8(h[k]);
-            if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
-        }
-    }
-
-    // ---- quantise (nothing more for a copy-only launch)
-    if constexpr (MODE == kNone) {
-        return;
-    } else if constexpr (MODE == kPT) {
-        if (has0) am0 = max_wave(am0);
-        if constexpr (NSEG > 1)
-            if (has1) am1 = max_wave(am1);
-        if (a.WPR > 1) {
-            if ((tid & 63) == 0) {
-                redm[0][wave] = am0;
-                if constexpr (NSEG > 1) redm[1][wave] = am1;
-            }
-            lds_barrier();
-            am0 = lds_rows_max<NSEG>(&redm[0][p0], &redm[1][p0], a.WPR, am1);
-        }
-        const Fp32Scale sc0 = fp32_scale(am0);
-        const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;
-#pragma unroll
+        // ---- residual add (h = round_dt(x + r), stored), sum of squares
+        float h[CPL][8];
+        float ss0 = 0.f, ss1 = 0.f;
+        double sd0 = 0.0, sd1 = 0.0; // F32Q
+    #pragma unroll
         for (int k = 0; k < CPL; ++k) {
             if (!ok[k]) continue;
-            const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
-            const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
-            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
-            if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
+            uint4 hp = xv[k];
+            if (has_res) {
+                float rf[8];
+                unpack8<DT>(xv[k], h[k]);
+                unpack8<DT>(rv[k], rf);
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
+                hp = pack8<DT>(h[k]);
+                stg_stream(a.res_out + rrow + lc[k] * 16, hp);
+            }
+            unpack8<DT>(hp, h[k]);
+            if constexpr (F32Q) {
+                double sd = 0.0;
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) sd = __builtin_fma((double)h[k][i], (double)h[k][i], sd);
+                if (NSEG > 1 && sg[k]) sd1 += sd;
+                else sd0 += sd;
+            } else {
+                if (NSEG > 1 && sg[k]) ss1 = sumsq8<DT>(hp, ss1);
+                else ss0 = sumsq8<DT>(hp, ss0);
+            }
+        }
+
+        // segments this wavefront holds chunks of (with SEGU a scalar fact; a
+        // segment it does not hold contributes zeros, so its reduction is skipped)
+        bool has0 = true, has1 = NSEG > 1;
+        if constexpr (NSEG > 1 && SEGU) {
+            has0 = false;
+            has1 = false;
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                if (sg[k]) has1 = true;
+                else has0 = true;
+            }
+        }
+
+        // ---- row reduction: DPP/permlane inside the wavefront, one LDS step
+        //      across the wavefronts of the row
+        // (LDS partials are segment-major: a row's partials are contiguous)
+        const int p0 = rib * a.WPR;
+        __shared__ float redm[2][kMaxBlock / 64];
+        float inv0, inv1;
+        if constexpr (F32Q) {
+            __shared__ double redd[2][kMaxBlock / 64];
+            if (has0) sd0 = sum_wave_f64(sd0);
+            if constexpr (NSEG > 1)
+                if (has1) sd1 = sum_wave_f64(sd1);
+            if (a.WPR > 1) {
+                if ((tid & 63) == 0) {
+                    redd[0][wave] = sd0;
+                    if constexpr (NSEG > 1) redd[1][wave] = sd1;
+                }
+                lds_barrier();
+                sd0 = lds_rows_sum_f64<NSEG>(&redd[0][p0], &redd[1][p0], a.WPR, sd1);
+            }
+            inv0 = (float)(1.0 / sqrt(sd0 / (double)a.seg[0].cols + (double)a.eps));
+            inv1 = NSEG > 1 ? (float)(1.0 / sqrt(sd1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
+        } else {
+            __shared__ float red[2][kMaxBlock / 64];
+            if (has0) ss0 = sum_wave(ss0);
+            if constexpr (NSEG > 1)
+                if (has1) ss1 = sum_wave(ss1);
+            if (a.WPR > 1) {
+                if ((tid & 63) == 0) {
+                    red[0][wave] = ss0;
+                    if constexpr (NSEG > 1) red[1][wave] = ss1;
+                }
+                lds_barrier();
+                ss0 = lds_rows_sum<NSEG>(&red[0][p0], &red[1][p0], a.WPR, ss1);
+            }
+            inv0 = rsqrt_nr(__builtin_fmaf(ss0, a.inv_cols0, a.eps));
+            inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(ss1, a.inv_cols1, a.eps)) : inv0;
+        }
+
+        // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
+        //      Gemma: g * inv = (1 + w) inv as one FMA.  F32Q: y = (h inv) g
+        //      in that order is kept in place of h (the quantiser's input), and
+        //      only the copy is rounded.
+        float am0 = 0.f, am1 = 0.f;
+    #pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k]) continue;
+            const float inv = sg[k] ? inv1 : inv0;
+            float wf[8];
+            unpack8<DT>(wv[k], wf);
+            if constexpr (F32Q) {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float g = GEMMA ? 1.0f + wf[i] : wf[i];
+                    h[k][i] = (h[k][i] * inv) * g;
+                }
+            } else {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
+            }
+            const uint4 up = F32Q ? pack8<DT>(h[k]) : round8<DT>(h[k]);
+            uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
+            const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
+            if (normed)
+                stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
+            if constexpr (MODE == kPT) {
+                const float m = amax8(h[k]);
+                if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
+            }
+        }
+
+        // ---- quantise (nothing more for a copy-only launch)
+        if constexpr (MODE == kNone) {
+            return;
+        } else if constexpr (MODE == kPT) {
+            if (has0) am0 = max_wave(am0);
+            if constexpr (NSEG > 1)
+                if (has1) am1 = max_wave(am1);
+            if (a.WPR > 1) {
+                if ((tid & 63) == 0) {
+                    redm[0][wave] = am0;
+                    if constexpr (NSEG > 1) redm[1][wave] = am1;
+                }
+                lds_barrier();
+                am0 = lds_rows_max<NSEG>(&redm[0][p0], &redm[1][p0], a.WPR, am1);
+            }
+            const Fp32Scale sc0 = fp32_scale(am0);
+            const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                if (!ok[k]) continue;
+                const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+                const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
+                stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+                if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
+            }
+        } else {
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                if (!ok[k]) continue; // uniform over every quant group
+                const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+                uint2 q;
+                if constexpr (MODE == kMX) {
+                    const uint32_t b = e8m0_of(max_quad(amax8(h[k])));
+                    q = mx_codes8(h[k], mx_inv_scale(b));
+                    if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b;
+                } else {
+                    const Fp32Scale sc = fp32_scale(max_row16(amax8(h[k])));
+                    q = fp32scale_codes8(h[k], sc);
+                    if ((lc[k] & 15) == 0)
+                        reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
+                }
+                stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+            }
         }
     } else {
-#pragma unroll
+        const int tid = threadIdx.x;
+        // rows are whole wavefronts: the wavefront, its row and everything
+        // derived from them are wavefront-uniform (kept in scalar registers)
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int rib = a.R == 1 ? 0 : (wave >> a.wpr_shift); // row within the block
+        const int t = tid - rib * a.NT;                       // lane within the row
+        const int tw = wave * 64 - rib * a.NT;                // t of the wavefront's lane 0
+        const int64_t row = (int64_t)blockIdx.x * a.R + rib;
+        const bool row_ok = row < a.M;
+        const bool has_res = a.res_in != nullptr;
+
+        // per-row bases.  Lanes off the row (past its last chunk, or in a row
+        // slot past M) load the first chunk of the last row instead and compute
+        // on it like every lane; only their stores are skipped.  No branch then
+        // skips a load or its use, so the compiler's waits on the vector memory
+        // counter stay exact (a load it has to assume pending would make it
+        // wait for every store in flight too).
+        const int64_t lrow = row_ok ? row : a.M - 1; // a row that exists
+        const uint8_t *xrow0 = a.seg[0].x + lrow * a.seg[0].x_pitch;
+        const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + lrow * a.seg[1].x_pitch : xrow0;
+        const int64_t rrow = row * a.C0 * 16;  // stores (row_ok only)
+        const int64_t rlrow = lrow * a.C0 * 16; // loads
+
+        // ---- issue every load of the row
+        uint4 xv[CPL], rv[CPL], wv[CPL];
+        bool ok[CPL];
+        int sg[CPL], lc[CPL];
+    #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-            if (!ok[k]) continue; // uniform over every quant group
-            const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
-            uint2 q;
-            if constexpr (MODE == kMX) {
-                const uint32_t b = e8m0_of(max_quad(amax8(h[k])));
-                q = mx_codes8(h[k], mx_inv_scale(b));
-                if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b;
+            const int c = t + k * a.NT;
+            ok[k] = row_ok && c < a.C;
+            if constexpr (NSEG == 1) {
+                sg[k] = 0;
+                lc[k] = c;
             } else {
-                const Fp32Scale sc = fp32_scale(max_row16(amax8(h[k])));
-                q = fp32scale_codes8(h[k], sc);
-                if ((lc[k] & 15) == 0)
-                    reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
+                sg[k] = (SEGU ? tw + k * a.NT : c) >= a.C0 ? 1 : 0;
+                lc[k] = c - (sg[k] ? a.C0 : 0);
             }
-            stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+            const bool in = c < a.C;                 // a chunk of the row (any row)
+            const int ls = in ? lc[k] : 0;           // the chunk this lane loads
+            const bool s1 = NSEG > 1 && in && sg[k]; // ... and its segment
+            xv[k] = ldg_stream((s1 ? xrow1 : xrow0) + ls * 16);
+            wv[k] = ldg<uint4>((s1 ? a.seg[1].w : a.seg[0].w) + ls * 16);
+            if (has_res) rv[k] = ldg_stream(a.res_in + rlrow + ls * 16);
+        }
+
+        // ---- residual add (h = round_dt(x + r), stored), squares.
+        //      The mean square is summed in an order fixed by the row width
+        //      alone, never by the launch's row shape, so that a row's outputs
+        //      do not depend on the shape (and through it on the row count):
+        //      each chunk's 8 squares in a fixed chain; each 64-chunk block of
+        //      the row (one slot of one wavefront, in every shape) by the fixed
+        //      wavefront tree; the blocks by a fixed tree over their index.
+        float h[CPL][8];
+        float sq[CPL];   // this lane's chunk of slot k: its sum of squares
+        double sqd[CPL]; // F32Q: the same in fp64 (each square exact)
+    #pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            uint4 hp = xv[k];
+            if (has_res) {
+                float rf[8];
+                unpack8<DT>(xv[k], h[k]);
+                unpack8<DT>(rv[k], rf);
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) h[k][i] += rf[i];
+                hp = pack8<DT>(h[k]);
+                if (ok[k]) stg_stream(a.res_out + rrow + lc[k] * 16, hp);
+            }
+            unpack8<DT>(hp, h[k]);
+            sq[k] = 0.f;
+            sqd[k] = 0.0;
+            if constexpr (F32Q) {
+                double d = 0.0;
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) d = __builtin_fma((double)h[k][i], (double)h[k][i], d);
+                sqd[k] = ok[k] ? d : 0.0;
+            } else {
+                const float f = sumsq8<DT>(hp, 0.f);
+                sq[k] = ok[k] ? f : 0.f;
+            }
+        }
+
+        // ---- row reduction.  Slot k of this wavefront is the aligned block
+        //      (tw + k NT) / 64 of the row.  Every block total goes to LDS at its
+        //      block index (0 for a segment the block holds no chunk of) and,
+        //      after one barrier, the blocks of each segment are added by
+        //      lds_blocks_sum.  With SEGU a slot lies in one segment, and the
+        //      other segment's reduction is skipped.
+        const int NB = (a.C + 63) >> 6; // blocks of the row (a function of the width)
+        const int pb = rib * NB;        // this row's first LDS entry
+        __shared__ float redm[2][kMaxBlock / 64];
+        float inv0, inv1;
+        auto slot_seg = [&](int k, int s) -> bool { // may slot k hold chunks of segment s
+            if constexpr (NSEG == 1) return s == 0;
+            else if constexpr (SEGU) return sg[k] == s;
+            else return true;
+        };
+        if constexpr (F32Q) {
+            __shared__ double redd[2][64];
+            double t0, t1;
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int b = (tw + k * a.NT) >> 6;
+                if (b >= NB) continue; // wavefront-uniform
+                double b0 = 0.0, b1 = 0.0;
+                if constexpr (NSEG == 1) {
+                    b0 = sum_wave_f64(sqd[k]);
+                } else {
+                    if (slot_seg(k, 0)) b0 = sum_wave_f64(sg[k] ? 0.0 : sqd[k]);
+                    if (slot_seg(k, 1)) b1 = sum_wave_f64(sg[k] ? sqd[k] : 0.0);
+                }
+                if ((tid & 63) == 0) {
+                    redd[0][pb + b] = b0;
+                    if constexpr (NSEG > 1) redd[1][pb + b] = b1;
+                }
+            }
+            lds_barrier();
+            t0 = lds_blocks_sum_f64<NSEG>(&redd[0][pb], &redd[1][pb], NB, t1);
+            inv0 = (float)(1.0 / sqrt(t0 / (double)a.seg[0].cols + (double)a.eps));
+            inv1 = NSEG > 1 ? (float)(1.0 / sqrt(t1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
+        } else {
+            __shared__ float red[2][64];
+            float t0, t1;
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int b = (tw + k * a.NT) >> 6;
+                if (b >= NB) continue; // wavefront-uniform
+                float b0 = 0.f, b1 = 0.f;
+                if constexpr (NSEG == 1) {
+                    b0 = sum_wave(sq[k]);
+                } else {
+                    if (slot_seg(k, 0)) b0 = sum_wave(sg[k] ? 0.f : sq[k]);
+                    if (slot_seg(k, 1)) b1 = sum_wave(sg[k] ? sq[k] : 0.f);
+                }
+                if ((tid & 63) == 0) {
+                    red[0][pb + b] = b0;
+                    if constexpr (NSEG > 1) red[1][pb + b] = b1;
+                }
+            }
+            lds_barrier();
+            t0 = lds_blocks_sum<NSEG>(&red[0][pb], &red[1][pb], NB, t1);
+            inv0 = rsqrt_nr(__builtin_fmaf(t0, a.inv_cols0, a.eps));
+            inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(t1, a.inv_cols1, a.eps)) : inv0;
+        }
+
+        // ---- u = round_dt(h * inv * g), kept in place of h; optional copy.
+        //      Gemma: g * inv = (1 + w) inv as one FMA.  F32Q: y = (h inv) g
+        //      in that order is kept in place of h (the quantiser's input), and
+        //      only the copy is rounded.
+        float am0 = 0.f, am1 = 0.f;
+    #pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const float inv = sg[k] ? inv1 : inv0;
+            float wf[8];
+            unpack8<DT>(wv[k], wf);
+            if constexpr (F32Q) {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float g = GEMMA ? 1.0f + wf[i] : wf[i];
+                    h[k][i] = (h[k][i] * inv) * g;
+                }
+            } else {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    h[k][i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
+            }
+            const uint4 up = F32Q ? pack8<DT>(h[k]) : round8<DT>(h[k]);
+            uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
+            const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
+            if (normed && ok[k])
+                stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up);
+            if constexpr (MODE == kPT) {
+                const float m = ok[k] ? amax8(h[k]) : 0.f;
+                if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
+            }
+        }
+
+        // ---- quantise (nothing more for a copy-only launch)
+        if constexpr (MODE == kNone) {
+            return;
+        } else if constexpr (MODE == kPT) {
+            // segments this wavefront holds chunks of (with SEGU a scalar fact; a
+            // segment it does not hold contributes zeros, so its max is skipped)
+            bool has0 = true, has1 = NSEG > 1;
+            if constexpr (NSEG > 1 && SEGU) {
+                has0 = false;
+                has1 = false;
+    #pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    if (sg[k]) has1 = true;
+                    else has0 = true;
+                }
+            }
+            if (has0) am0 = max_wave(am0);
+            if constexpr (NSEG > 1)
+                if (has1) am1 = max_wave(am1);
+            const int p0 = rib * a.WPR; // this row's first wavefront in the block
+            if (a.WPR > 1) {
+                if ((tid & 63) == 0) {
+                    redm[0][wave] = am0;
+                    if constexpr (NSEG > 1) redm[1][wave] = am1;
+                }
+                lds_barrier();
+                am0 = lds_rows_max<NSEG>(&redm[0][p0], &redm[1][p0], a.WPR, am1);
+            }
+            const Fp32Scale sc0 = fp32_scale(am0);
+            const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(am1) : sc0;
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                if (!ok[k]) continue;
+                const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+                const uint2 q = fp32scale_codes8(h[k], sg[k] ? sc1 : sc0);
+                stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+                if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
+            }
+        } else {
+            uint2 q[CPL];
+            uint32_t b[CPL];
+            Fp32Scale sc[CPL];
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) { // lanes off the row: their own groups only
+                if constexpr (MODE == kMX) {
+                    b[k] = e8m0_of(max_quad(amax8(h[k])));
+                    q[k] = mx_codes8(h[k], mx_inv_scale(b[k]));
+                } else {
+                    sc[k] = fp32_scale(max_row16(amax8(h[k])));
+                    q[k] = fp32scale_codes8(h[k], sc[k]);
+                }
+            }
+    #pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                if (!ok[k]) continue;
+                const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+                if constexpr (MODE == kMX) {
+                    if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b[k];
+                } else {
+                    if ((lc[k] & 15) == 0)
+                        reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc[k].s;
+                }
+                stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q[k]);
+            }
         }
     }
 }
@@ -334,7 +594,8 @@ int launch_norm(const NormPlan &p, void *stream)
     a.C0 = p.seg[0].chunks;
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
     const int mode = p.quant ? p.mode : kNone;
-    const RowShapeRt sh = row_shape(a.C, p.M, mode == kPT);
+    const bool copy = p.seg[0].normed != nullptr || (p.nseg > 1 && p.seg[1].normed != nullptr);
+    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode, copy);
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;

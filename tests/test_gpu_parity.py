@@ -118,13 +118,70 @@ def test_two_segment_per_token(dtype, M):
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
 @pytest.mark.parametrize("H", [4096, 6144])
 def test_norm_bandwidth_row_counts(mode, H):
-    """Above 1024 rows a launch takes the bandwidth-bound row shape (two
-    chunks per lane for per-token rows): every row against the oracle."""
+    """1100 rows: the per-token launch takes two (width 4096) or three (6144)
+    chunks per lane, the MXFP8 launch with the copy two (1x128 one): every
+    row against the oracle."""
     M = 1100
     d = inputs.norm_inputs(M, H, seed=8, x_std=2.0, r_std=1.0, w_kind="normal", w_param=0.1)
     gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
     ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode)
     _report(f"bandwidth rows {mode} H={H}", check_norm(gpu, ref, mode, "bf16", f"bw-{mode}"))
+
+
+@pytest.mark.parametrize("mode,H,M,dtype", [
+    ("mx", 6144, 1536, "bf16"),   # three chunks per lane
+    ("mx", 4096, 3072, "bf16"),   # four chunks per lane, two rows of 128 lanes per block
+    ("mx", 8192, 1536, "fp16"),   # four chunks per lane, 256 lanes
+    ("mx", 2048, 3072, "bf16"),   # two chunks per lane, two rows per block
+    ("pt", 6144, 300, "bf16"),    # above 256 rows: three chunks per lane
+    ("pt", 8192, 64, "fp16"),     # up to 256 rows: two chunks per lane, 512 lanes
+    ("pt", 2048, 257, "bf16"),    # two chunks per lane, two rows per block, a ragged block
+])
+def test_norm_row_shapes_by_size(mode, H, M, dtype):
+    """The row shapes the launcher picks by row count (MXFP8 with the copy
+    at two or three rounds of rows; per-token at every size): every row
+    against the oracle, with the copy."""
+    print(f"case row shape {mode} H={H} M={M} {dtype}", flush=True)
+    d = inputs.norm_inputs(M, H, seed=13, x_std=2.0, r_std=1.0, w_kind="normal", w_param=0.1,
+                           dtype=dtype)
+    gpu = run_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode, dtype=dtype)
+    ref = ref_norm(d["x"], d["w"], r=d["r"], kind="gemma", mode=mode, dtype=dtype)
+    _report(f"row shape {mode} H={H} M={M}", check_norm(gpu, ref, mode, dtype, f"shape-{mode}"))
+
+
+@pytest.mark.parametrize("mode,H,Ms,qin", [
+    ("pt", 6144, (8, 300, 1100), 0),     # 2, 3, 3 chunks per lane
+    ("pt", 2048, (8, 300, 1100), 0),     # 1 chunk per lane, then 2 with two rows per block
+    ("pt", 8192, (8, 300), 1),           # fp32-direct: 2 chunks per lane, 512 then 512 lanes
+    ("mx", 6144, (8, 1024, 1536), 0),    # 1, 2, 3 chunks per lane
+    ("mx", 4096, (8, 1536, 3072), 0),    # 1, 2, 4 chunks per lane (two rows per block)
+    ("b128", 4096, (8, 1100), 1),        # fp32-direct 1x128: 1 chunk per lane
+])
+def test_rows_independent_of_launch_shape(mode, H, Ms, qin):
+    """The row shape depends on the row count, but the mean square is summed
+    in an order fixed by the width: the first 8 rows come out bit-identical
+    from launches of every row count and from the copy-only launch (one
+    chunk per lane), residual and copy included."""
+    print(f"case shape invariance {mode} H={H} Ms={Ms} qin={qin}", flush=True)
+    Mmax = max(Ms)
+    d = inputs.norm_inputs(Mmax, H, seed=17, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    first = None
+    for M in Ms:
+        g = run_norm(d["x"][:M], d["w"], r=d["r"][:M], kind="gemma", mode=mode, qin=qin)
+        rows = {k: np.ascontiguousarray(g[k][:8]) for k in ("h", "normed", "values", "scales")}
+        if first is None:
+            first = rows
+            ref = ref_norm(d["x"][:8], d["w"], r=d["r"][:8], kind="gemma", mode=mode, qin=qin)
+            check_norm(g, ref, mode, "bf16", f"shape-inv-{mode}", requant=(qin == 0))
+        for k in rows:
+            assert np.array_equal(rows[k], first[k]), (M, k)
+    x, w, r = dev16(d["x"][:300]), dev16(d["w"]), dev16(d["r"][:300])
+    plain = afq.fused_add_rmsnorm_quant(x, w, 1e-6, mode=MODE[mode], kind=afq.GEMMA, residual=r,
+                                        quantize=False)
+    torch.cuda.synchronize()
+    if qin == 0:
+        assert np.array_equal(host16(plain.normed)[:8], first["normed"])
+    assert np.array_equal(host16(plain.residual)[:8], first["h"])
 
 
 @pytest.mark.parametrize("H", [20480, 32768])
