@@ -64,14 +64,14 @@ static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
 }
 
 // Rows of the norm kernel that one round of the GPU holds at cpl chunks per
-// lane: 256 CUs, each with 32 wavefront slots (8 per SIMD; 7 at four chunks
-// per lane, where the kernel needs more than 64 VGPRs), whole rows per CU.
-constexpr int64_t kCUs = 256;
-static inline int64_t norm_rows_per_round(int C, int cpl)
+// lane: `cus` compute units (256 on a whole MI355X), each with 32 wavefront
+// slots (8 per SIMD; 7 at four chunks per lane, where the kernel needs more
+// than 64 VGPRs), whole rows per CU.
+static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 {
     const int waves = row_lanes(C, cpl) / 64;
     const int slots = cpl >= 4 ? 28 : 32;
-    return kCUs * (slots / waves);
+    return cus * (slots / waves);
 }
 
 // The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
@@ -91,7 +91,7 @@ static inline int64_t norm_rows_per_round(int C, int cpl)
 //    launch is bandwidth-bound and longer lane work only costs);
 //  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
 //    per lane, which the same sweep found best for 1x128 at every size.
-static inline RowShapeRt norm_row_shape(int C, int64_t M, int mode, bool copy)
+static inline RowShapeRt norm_row_shape(int C, int64_t M, int mode, bool copy, int64_t cus)
 {
     int cpl = 1;
     if (mode == kPT) {
@@ -106,10 +106,10 @@ static inline RowShapeRt norm_row_shape(int C, int64_t M, int mode, bool copy)
                 }
         }
     } else if (mode == kMX && copy) {
-        const int64_t r1 = norm_rows_per_round(C, 1);
+        const int64_t r1 = norm_rows_per_round(C, 1, cus);
         if (M > r1 && M <= 3 * r1)
             for (int c = 2; c <= 4; ++c)
-                if (norm_rows_per_round(C, c) >= M) {
+                if (norm_rows_per_round(C, c, cus) >= M) {
                     cpl = c;
                     break;
                 }

@@ -13,6 +13,8 @@
 #include "afq_internal.h"
 #include "afq_launch.hpp"
 
+#include <atomic>
+
 namespace afq {
 
 // Rows are NT lanes (a whole number of wavefronts, NT <= 1024); a block
@@ -582,6 +584,24 @@ static hipError_t go_norm_mode(const NormArgs &a, int mode, bool f32q, bool gemm
     }
 }
 
+// Compute units of the current device (the device the binding and the C
+// callers launch on), read once per device: the row-shape rule counts whole
+// rows per CU, and a partitioned MI355X exposes fewer than 256 per device.
+static int64_t device_cus()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices]; // 0: not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 int launch_norm(const NormPlan &p, void *stream)
 {
     NormArgs a;
@@ -595,7 +615,7 @@ int launch_norm(const NormPlan &p, void *stream)
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
     const int mode = p.quant ? p.mode : kNone;
     const bool copy = p.seg[0].normed != nullptr || (p.nseg > 1 && p.seg[1].normed != nullptr);
-    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode, copy);
+    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode, copy, device_cus());
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;
