@@ -517,6 +517,9 @@ PROFILE_WORKLOADS = {
     "norm_b128_h4096": lambda: _prof_norm_b128(),
     "norm_b128_f32q_h4096": lambda: _prof_norm_b128(qin=1),
     "twoseg_pt_m8192": lambda: TwoSegCase(8192, seed=0, sets=rotation_sets(two_seg_bytes(8192))),
+    "norm_mx_m1024": lambda: NormCase(1024, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal",
+                                      w_param=0.1, kind="gemma", mode="mx",
+                                      sets=rotation_sets(norm_bytes(1024, 6144))),
     "silu_b128_i12288": lambda: SiluCase(4096, 12288, seed=0, std=1.0, mode="b128",
                                          sets=rotation_sets(silu_bytes(4096, 12288, mode="b128"))),
     "silu_b128_i3072": lambda: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128",
