@@ -326,9 +326,12 @@ norm_quant_kernel(const NormArgs a)
                 sg[k] = (SEGU ? tw + k * a.NT : c) >= a.C0 ? 1 : 0;
                 lc[k] = c - (sg[k] ? a.C0 : 0);
             }
-            const bool in = c < a.C;                 // a chunk of the row (any row)
-            const int ls = in ? lc[k] : 0;           // the chunk this lane loads
-            const bool s1 = NSEG > 1 && in && sg[k]; // ... and its segment
+            const bool in = c < a.C;       // a chunk of the row (any row)
+            const int ls = in ? lc[k] : 0; // the chunk this lane loads
+            // ... and its segment: with SEGU the slot's (wavefront-uniform,
+            // so the pointers are chosen in scalar registers; a lane past
+            // the row loads chunk 0 of that segment)
+            const bool s1 = NSEG > 1 && (SEGU ? sg[k] != 0 : (in && sg[k] != 0));
             xv[k] = ldg_stream((s1 ? xrow1 : xrow0) + ls * 16);
             wv[k] = ldg<uint4>((s1 ? a.seg[1].w : a.seg[0].w) + ls * 16);
             if (has_res) rv[k] = ldg_stream(a.res_in + rlrow + ls * 16);
