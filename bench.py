@@ -465,7 +465,7 @@ def run_sweep():
         fz["codes_differ_vs_chain"] = round((f.values.view(torch.uint8) != q.values.view(torch.uint8))
                                             .float().mean().item(), 4)
         fz["scales_differ_vs_chain"] = round((f.scales != q.scales).float().mean().item(), 4)
-    for M in (256, 1024):
+    for M in (256, 1024, 2048):
         rec("C1", c1, norm_c1(M), M, norm_bytes(M, 6144))
     for M in (1, 32, 256, 4096):
         rec("C3a", "add + standard RMSNorm + 1x128, H=4096",
