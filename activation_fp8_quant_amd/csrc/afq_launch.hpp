@@ -1,133 +1,20 @@
-// afq_launch.hpp -- launch-shape helpers shared by the kernel launchers:
-// the row shape of the row kernels, the rows per launch of the flat
-// kernels, and the flat kernels' division of a chunk index by the chunks
-// per row (multiplier made on the host, applied on the device).
+// afq_launch.hpp -- launch helpers shared by the kernel launchers: the
+// launch-shape rules (afq_shape.hpp), the device half of the flat kernels'
+// division of a chunk index by the chunks per row, and buffer offsets.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "afq_shape.hpp"
+
 namespace afq {
 
-// Division of a flat 32-bit chunk index by the chunks per row C, by a
-// multiplier computed on the host (round-up method): with l = ceil(log2 C)
-// and m = floor(2^32 (2^l - C) / C) + 1, n / C = (mulhi(n, m) + n) >> l
-// for every n < 2^32 (the sum is taken in 64 bits).
-struct DivC {
-    uint32_t m;
-    uint32_t l;
-};
-static inline DivC divc(uint32_t C)
-{
-    uint32_t l = 0;
-    while ((1ull << l) < C) ++l;
-    DivC d;
-    d.m = (uint32_t)(((1ull << 32) * ((1ull << l) - C)) / C + 1);
-    d.l = l;
-    return d;
-}
+// The flat kernels' division of a chunk index by C: the multiplier and
+// shift come from divc() on the host (afq_shape.hpp).
 __device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
 {
     return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
-}
-
-// Row shapes of the row kernels.  A row of C chunks runs on NT lanes (a
-// whole number of wavefronts, at most 1024), CPL = ceil(C / NT) chunks per
-// lane; rows of fewer than 256 lanes are packed several to a block.
-struct RowShapeRt {
-    int NT, CPL, R, WPR;
-};
-static inline int row_lanes(int C, int cpl)
-{
-    const int nt = (C + cpl - 1) / cpl;
-    return (nt + 63) / 64 * 64;
-}
-static inline RowShapeRt shape_at(int C, int cpl)
-{
-    if ((C + cpl - 1) / cpl > 1024) cpl = (C + 1023) / 1024;
-    RowShapeRt s;
-    const int nt = row_lanes(C, cpl);
-    s.NT = nt;
-    s.CPL = (C + nt - 1) / nt;
-    s.R = (nt < 256 && 256 % nt == 0) ? 256 / nt : 1;
-    s.WPR = nt / 64;
-    return s;
-}
-
-// The standalone per-token quantiser: one chunk per lane (as many lanes as
-// chunks, up to 1024), so that a row's loads are all in flight at once and
-// the per-lane work is shortest, except in launches above 1024 rows, which
-// take two chunks per lane.
-static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
-{
-    return shape_at(C, (per_token && M > 1024) ? 2 : 1);
-}
-
-// Rows of the norm kernel that one round of the GPU holds at cpl chunks per
-// lane: `cus` compute units (256 on a whole MI355X), each with 32 wavefront
-// slots (8 per SIMD; 7 at four chunks per lane, where the kernel needs more
-// than 64 VGPRs), whole rows per CU.
-static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
-{
-    const int waves = row_lanes(C, cpl) / 64;
-    const int slots = cpl >= 4 ? 28 : 32;
-    return cus * (slots / waves);
-}
-
-// The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
-// 2048 / 4096 / 6144 / 8192, 1 to 4096 rows, one to four chunks per lane):
-//  * per-token (two row reductions, each an LDS exchange across the row's
-//    wavefronts): up to 256 rows, rows of 256 to 512 lanes (two chunks per
-//    lane for rows wider than 2048; 7-23 % faster at widths 4096-8192, 8
-//    rows); above 256 rows, the fewest chunks per lane from two up whose
-//    row is a whole divisor of a CU's 32 wavefront slots (13-44 % faster
-//    than one chunk per lane from 512 rows: at width 6144, 4096 rows,
-//    27.6 -> 15.4 us at three chunks per lane);
-//  * MXFP8 with the copy: when one chunk per lane needs two or three rounds
-//    of rows, the fewest chunks per lane that hold every row in one round
-//    (7-13 % faster: width 6144, 1024 rows 12.8 -> 11.3 us; width 4096,
-//    3072 rows 21.7 -> 20.2 us at four chunks per lane); one chunk per lane
-//    otherwise (at one round it is as fast, at four or more rounds the
-//    launch is bandwidth-bound and longer lane work only costs);
-//  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
-//    per lane, which the same sweep found best for 1x128 at every size.
-static inline RowShapeRt norm_row_shape(int C, int64_t M, int mode, bool copy, int64_t cus)
-{
-    int cpl = 1;
-    if (mode == kPT) {
-        if (M <= 256) {
-            cpl = C > 256 ? 2 : 1;
-        } else {
-            cpl = 2;
-            for (int c = 2; c <= 4; ++c)
-                if (32 % (row_lanes(C, c) / 64) == 0) {
-                    cpl = c;
-                    break;
-                }
-        }
-    } else if (mode == kMX && copy) {
-        const int64_t r1 = norm_rows_per_round(C, 1, cus);
-        if (M > r1 && M <= 3 * r1)
-            for (int c = 2; c <= 4; ++c)
-                if (norm_rows_per_round(C, c, cus) >= M) {
-                    cpl = c;
-                    break;
-                }
-    }
-    return shape_at(C, cpl);
-}
-
-// Rows per launch of the flat kernels: the flat chunk index stays below
-// 2^31 (larger M is covered by several launches over row slices).
-static inline int64_t flat_rows_per_launch(int32_t C) { return ((int64_t)1 << 31) / C; }
-
-// Rows per launch of the row kernels (NT lanes per row, R rows per block):
-// a launch stays below 2^31 work-items (a dispatch's grid size is a 32-bit
-// count of work-items), a whole number of blocks; larger M is covered by
-// several launches over row slices.
-static inline int64_t row_rows_per_launch(int NT, int R)
-{
-    return (((int64_t)1 << 31) / NT) / R * R;
 }
 
 // Bytes of scales per row of `cols` elements in quant mode `mode`.

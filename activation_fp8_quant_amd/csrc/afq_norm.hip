@@ -618,7 +618,7 @@ int launch_norm(const NormPlan &p, void *stream)
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
     const int mode = p.quant ? p.mode : kNone;
     const bool copy = p.seg[0].normed != nullptr || (p.nseg > 1 && p.seg[1].normed != nullptr);
-    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode, copy, device_cus());
+    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode == kPT, mode == kMX && copy, device_cus());
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;

@@ -91,7 +91,7 @@ def _dev16(bits, dtype="bf16"):
 
 def _src_hash():
     h = hashlib.sha256()
-    for f in ("afq_norm.hip", "afq_device.hpp", "afq_launch.hpp"):
+    for f in ("afq_norm.hip", "afq_device.hpp", "afq_launch.hpp", "afq_shape.hpp"):
         with open(os.path.join(ROOT, "activation_fp8_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -136,6 +136,9 @@ def test_norm_bandwidth_row_counts(mode, H):
     ("pt", 6144, 300, "bf16"),    # above 256 rows: three chunks per lane
     ("pt", 8192, 64, "fp16"),     # up to 256 rows: two chunks per lane, 512 lanes
     ("pt", 2048, 257, "bf16"),    # two chunks per lane, two rows per block, a ragged block
+    ("mx", 16384, 600, "bf16"),   # wider than 1024 chunks: base two per lane, one round at four
+    ("mx", 8224, 1000, "bf16"),   # 1028 chunks: base two per lane (576 lanes), one round at three
+    ("pt", 16384, 300, "fp16"),   # per-token above 256 rows at two chunks per lane, 1024 lanes
 ])
 def test_norm_row_shapes_by_size(mode, H, M, dtype):
     """The row shapes the launcher picks by row count (MXFP8 with the copy
@@ -156,6 +159,7 @@ def test_norm_row_shapes_by_size(mode, H, M, dtype):
     ("mx", 6144, (8, 1024, 1536), 0),    # 1, 2, 3 chunks per lane
     ("mx", 4096, (8, 1536, 3072), 0),    # 1, 2, 4 chunks per lane (two rows per block)
     ("b128", 4096, (8, 1100), 1),        # fp32-direct 1x128: 1 chunk per lane
+    ("mx", 16384, (8, 600, 1000), 0),    # 2 (1024 lanes), 4 (512 lanes), 2 chunks per lane
 ])
 def test_rows_independent_of_launch_shape(mode, H, Ms, qin):
     """The row shape depends on the row count, but the mean square is summed

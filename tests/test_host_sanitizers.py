@@ -1,11 +1,15 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU).
 
-Two standalone programs are built with g++/gcc and the sanitizers, with no
+Three standalone programs are built with g++/gcc and the sanitizers, with no
 HIP code in them:
   * abi_fuzz: the C ABI's validation (afq_abi.cpp) against stub launchers
     that check the invariants the kernels rely on, over 200,000 random
     descriptors (valid and invalid sizes, strides, pointers, enums);
-  * oracle_run: every path of the CPU oracle on random and edge-case rows.
+  * oracle_run: every path of the CPU oracle on random and edge-case rows;
+  * shape_check: the launch-shape rules (afq_shape.hpp) over every row width
+    and a spread of row counts and compute-unit counts, against what the
+    kernels assume of a shape, the rule's measured picks, and the flat
+    kernels' division by the chunks per row against exact division.
 Any sanitizer report, violated invariant or undocumented status fails.
 """
 import os
@@ -48,3 +52,14 @@ def test_oracle_paths(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     assert "runtime error" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr
     assert "oracle paths ok" in r.stdout
+
+
+def test_launch_shapes(tmp_path):
+    exe = str(tmp_path / "shape_check")
+    b = _run(["g++", "-std=c++17", *SAN, f"-I{ROOT}/activation_fp8_quant_amd/csrc",
+              f"{HERE}/shape_check.cpp", "-o", exe])
+    assert b.returncode == 0, b.stderr
+    r = _run([exe], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "runtime error" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr
+    assert "launch shapes ok" in r.stdout
