@@ -17,6 +17,9 @@ __device__ __forceinline__ uint32_t div_c(uint32_t n, DivC d)
     return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
 }
 
+// Compute units of the current device, read once per device (afq_norm.hip).
+int64_t device_cus();
+
 // Bytes of scales per row of `cols` elements in quant mode `mode`.
 static inline int64_t scale_row_bytes(int mode, int32_t cols)
 {

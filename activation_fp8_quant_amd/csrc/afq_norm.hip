@@ -588,9 +588,9 @@ static hipError_t go_norm_mode(const NormArgs &a, int mode, bool f32q, bool gemm
 }
 
 // Compute units of the current device (the device the binding and the C
-// callers launch on), read once per device: the row-shape rule counts whole
+// callers launch on), read once per device: the row-shape rules count whole
 // rows per CU, and a partitioned MI355X exposes fewer than 256 per device.
-static int64_t device_cus()
+int64_t device_cus()
 {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices]; // 0: not read yet

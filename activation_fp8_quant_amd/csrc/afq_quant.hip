@@ -142,7 +142,7 @@ template <int DT>
 static hipError_t go_quant(QuantArgs &a, int mode, hipStream_t st)
 {
     if (mode == kPT) {
-        const RowShapeRt sh = row_shape(a.C, a.M, true);
+        const RowShapeRt sh = quant_row_shape(a.C, a.M, device_cus());
         a.NT = sh.NT;
         a.R = sh.R;
         a.WPR = sh.WPR;

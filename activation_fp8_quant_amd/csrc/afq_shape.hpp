@@ -50,13 +50,42 @@ static inline RowShapeRt shape_at(int C, int cpl)
     return s;
 }
 
-// The standalone per-token quantiser: one chunk per lane (as many lanes as
-// chunks, up to 1024), so that a row's loads are all in flight at once and
-// the per-lane work is shortest, except in launches above 1024 rows, which
-// take two chunks per lane.
-static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
+// Rows of a row kernel that one round of the GPU holds in the row shape
+// shape_at(C, cpl): `cus` compute units (256 on a whole MI355X), `slots`
+// wavefront slots per CU, whole rows per CU.
+static inline int64_t rows_per_round(int C, int cpl, int slots, int64_t cus)
 {
-    return shape_at(C, (per_token && M > 1024) ? 2 : 1);
+    return cus * (slots / shape_at(C, cpl).WPR);
+}
+
+// The standalone per-token quantiser's row shape (its kernel runs 8
+// wavefronts per SIMD, 32 per CU, at one to four chunks per lane), chosen
+// from a sweep (graph replay, rotated buffers, widths 2048 / 4096 / 6144 /
+// 8192, 1 to 8192 rows, one to four chunks per lane):
+//  * up to 256 rows: two chunks per lane for rows wider than 4096 (10-22 %
+//    faster at widths 6144 and 8192 up to 64 rows), one otherwise;
+//  * above 256 rows: one chunk per lane while a round at one chunk per lane
+//    holds more rows than the launch; otherwise the fewest chunks per lane,
+//    from two up, whose round holds every row (width 6144 at 1024 rows
+//    7.6 -> 5.1 us, width 8192 at 512 rows 5.7 -> 4.4 us, width 4096 at 4096
+//    rows 10.8 -> 9.5 us); four when no round holds them all.
+// Over the sweep's 40 launches this takes 261 us against 276 us for the
+// earlier rule (one chunk per lane up to 1024 rows, two above) and 258 us
+// for the best shape of each launch.
+static inline RowShapeRt quant_row_shape(int C, int64_t M, int64_t cus)
+{
+    int cpl = 1;
+    if (M <= 256) {
+        cpl = C > 512 ? 2 : 1;
+    } else if (rows_per_round(C, 1, 32, cus) <= M) {
+        cpl = 4;
+        for (int c = 2; c < 4; ++c)
+            if (rows_per_round(C, c, 32, cus) >= M) {
+                cpl = c;
+                break;
+            }
+    }
+    return shape_at(C, cpl);
 }
 
 // Rows of the norm kernel that one round of the GPU holds in the row shape
@@ -66,9 +95,7 @@ static inline RowShapeRt row_shape(int C, int64_t M, bool per_token)
 // lane, where the kernel needs more than 64 VGPRs), whole rows per CU.
 static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 {
-    const RowShapeRt s = shape_at(C, cpl);
-    const int slots = s.CPL >= 4 ? 28 : 32;
-    return cus * (slots / s.WPR);
+    return rows_per_round(C, cpl, shape_at(C, cpl).CPL >= 4 ? 28 : 32, cus);
 }
 
 // The norm kernel's row shape, chosen from a sweep (rotated buffers, widths

@@ -501,10 +501,11 @@ def test_fp8_quant_mx_every_fp16_value_under_every_block_exponent():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("n", [3072, 20480, 32768])
+@pytest.mark.parametrize("n", [3072, 6144, 8192, 20480, 32768])
 def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
-    """The standalone per-token quantiser above 1024 rows (two chunks per
-    lane, three at 20480, four at 32768): 1100 rows, bit-exact."""
+    """The standalone per-token quantiser at 1100 rows, where its row shape
+    takes one chunk per lane at width 3072 (one round holds every row), two
+    at 6144, three at 8192 and four at 20480 and 32768: bit-exact."""
     rng = np.random.default_rng(11)
     M = 1100
     x = rng.standard_normal((M, n)) * 2.0 ** rng.integers(-8, 8, (M, 1))
@@ -521,6 +522,24 @@ def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
     q, s = orc.quant(xh, odt, afq.PER_TOKEN, threads=8)
     assert np.array_equal(host8(qa.values), q)
     assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint32), s.view(np.uint32))
+
+
+def test_fp8_quant_per_token_rows_independent_of_shape():
+    """The standalone per-token quantiser's row shape follows the row count
+    (width 8192: two chunks per lane at 8 rows, one at 300, three at 1100,
+    four at 2048): the first 8 rows come out bit-identical from every launch, and
+    equal to the oracle's."""
+    rng = np.random.default_rng(23)
+    n = 8192
+    xh = inputs.to_bits(rng.standard_normal((2048, n)) * 2.0 ** rng.integers(-8, 8, (2048, 1)), "bf16")
+    xt = dev16(xh, "bf16")
+    q, s = orc.quant(xh[:8], ORC_DT["bf16"], afq.PER_TOKEN, threads=8)
+    for M in (8, 300, 1100, 2048):
+        print(f"case per-token quant shape M={M}", flush=True)
+        qa = afq.fp8_quant(xt[:M], afq.PER_TOKEN)
+        torch.cuda.synchronize()
+        assert np.array_equal(host8(qa.values)[:8], q), M
+        assert np.array_equal(scales_u8_or_f32(qa.scales)[:8].view(np.uint32), s.view(np.uint32)), M
 
 
 @pytest.mark.parametrize("mode", ["mx", "b128", "pt"])
