@@ -524,6 +524,8 @@ PROFILE_WORKLOADS = {
                                          sets=rotation_sets(silu_bytes(4096, 12288, mode="b128"))),
     "silu_b128_i3072": lambda: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128",
                                         sets=rotation_sets(silu_bytes(16384, 3072, mode="b128"))),
+    "quant_pt_h8192_m1024": lambda: QuantCase(1024, 8192, seed=0, std=3.0, mode="pt",
+                                              sets=rotation_sets(1024 * 3 * 8192)),
     # decode sizes, hot (one buffer set), launched by graph replay as the
     # sweep times them
     "norm_mx_m8": lambda: NormCase(8, 6144, seed=0, x_std=3.0, r_std=1.0, w_kind="normal",
@@ -531,8 +533,9 @@ PROFILE_WORKLOADS = {
     "silu_mx_i768_m8": lambda: SiluCase(8, 768, seed=0, std=2.0, mode="mx"),
     "swiglu_mx_i768_m8": lambda: SiluCase(8, 768, seed=0, std=8.0, mode="mx",
                                           swiglu=(1.702, 1.0, 7.0)),
+    "quant_mx_h6144_m8": lambda: QuantCase(8, 6144, seed=0, std=3.0, mode="mx"),
 }
-PROFILE_BY_GRAPH = {"norm_mx_m8", "silu_mx_i768_m8", "swiglu_mx_i768_m8"}
+PROFILE_BY_GRAPH = {"norm_mx_m8", "silu_mx_i768_m8", "swiglu_mx_i768_m8", "quant_mx_h6144_m8"}
 
 
 def replay_launches(fn, launches, per_graph=200):
