@@ -94,15 +94,23 @@ quant_row_kernel(const QuantArgs a)
     float v[CPL][8];
     bool ok[CPL];
     float am = 0.f;
+    // Every lane loads, without a branch: a lane off the rows or past the
+    // row's end reads an in-bounds chunk (the last row's, the row's last)
+    // and leaves it out of the max and the stores.  Loads under a lane mask
+    // made the compiler wait for each before issuing the next.
+    const int64_t lrow = row_ok ? row : a.M - 1;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const int c = t + k * a.NT;
         ok[k] = row_ok && c < a.C;
-        if (ok[k]) load_chunk<DT>(a.x + row * a.x_pitch + (int64_t)c * 8 * EB, v[k]);
+        const int lc = c < a.C ? c : a.C - 1;
+        load_chunk<DT>(a.x + lrow * a.x_pitch + (int64_t)lc * 8 * EB, v[k]);
     }
 #pragma unroll
-    for (int k = 0; k < CPL; ++k)
-        if (ok[k]) am = __builtin_fmaxf(am, amax8(v[k]));
+    for (int k = 0; k < CPL; ++k) {
+        const float m = amax8(v[k]);
+        am = ok[k] ? __builtin_fmaxf(am, m) : am;
+    }
     am = max_wave(am);
     __shared__ float redm[kMaxBlock / 64];
     if (a.WPR > 1) {

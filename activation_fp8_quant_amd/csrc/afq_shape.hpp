@@ -61,31 +61,16 @@ static inline int64_t rows_per_round(int C, int cpl, int slots, int64_t cus)
 // The standalone per-token quantiser's row shape (its kernel runs 8
 // wavefronts per SIMD, 32 per CU, at one to four chunks per lane), chosen
 // from a sweep (graph replay, rotated buffers, widths 2048 / 4096 / 6144 /
-// 8192, 1 to 8192 rows, one to four chunks per lane):
-//  * up to 256 rows: two chunks per lane for rows wider than 4096 (10-22 %
-//    faster at widths 6144 and 8192 up to 64 rows), one otherwise;
-//  * above 256 rows: one chunk per lane while a round at one chunk per lane
-//    holds more rows than the launch; otherwise the fewest chunks per lane,
-//    from two up, whose round holds every row (width 6144 at 1024 rows
-//    7.6 -> 5.1 us, width 8192 at 512 rows 5.7 -> 4.4 us, width 4096 at 4096
-//    rows 10.8 -> 9.5 us); four when no round holds them all.
-// Over the sweep's 40 launches this takes 261 us against 276 us for the
-// earlier rule (one chunk per lane up to 1024 rows, two above) and 258 us
-// for the best shape of each launch.
+// 8192, 1 to 8192 rows, one to four chunks per lane): two chunks per lane,
+// or three when a round at two chunks per lane cannot hold every row.  Over
+// the sweep's 40 launches this takes 243 us, against 242 us for the best
+// shape of each launch (at most 3.4 % slower in any one) and 248 us for
+// one chunk per lane up to 256 rows at widths up to 4096 and wherever a
+// round at one chunk per lane has rows to spare (the rule this replaced:
+// up to 20 % slower than two, e.g. width 4096 at 512 rows 3.85 -> 3.21 us).
 static inline RowShapeRt quant_row_shape(int C, int64_t M, int64_t cus)
 {
-    int cpl = 1;
-    if (M <= 256) {
-        cpl = C > 512 ? 2 : 1;
-    } else if (rows_per_round(C, 1, 32, cus) <= M) {
-        cpl = 4;
-        for (int c = 2; c < 4; ++c)
-            if (rows_per_round(C, c, 32, cus) >= M) {
-                cpl = c;
-                break;
-            }
-    }
-    return shape_at(C, cpl);
+    return shape_at(C, rows_per_round(C, 2, 32, cus) >= M ? 2 : 3);
 }
 
 // Rows of the norm kernel that one round of the GPU holds in the row shape

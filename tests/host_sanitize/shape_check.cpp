@@ -78,20 +78,12 @@ int main()
             for (long long cus : cuss) {
                 const RowShapeRt s = quant_row_shape(C, M, cus);
                 check_shape(s, C, "quant_row_shape", M, cus);
-                const int base = shape_at(C, 1).CPL;
-                if (M > 256 && s.CPL > base) { // more chunks per lane only when one round at the base is full
-                    CHECK(rows_per_round(C, base, 32, cus) <= M, "quant C=%d M=%lld cus=%lld CPL=%d", C, M, cus,
-                          s.CPL);
-                    // the fewest that hold every row in one round, or the shape asked for at four
-                    const RowShapeRt s4 = shape_at(C, 4);
-                    CHECK(rows_per_round(C, s.CPL, 32, cus) >= M || (s.NT == s4.NT && s.CPL == s4.CPL),
-                          "quant C=%d M=%lld CPL=%d", C, M, s.CPL);
-                    for (int c = 2; c < s.CPL; ++c)
-                        CHECK(rows_per_round(C, c, 32, cus) < M || shape_at(C, c).CPL == s.CPL,
-                              "quant C=%d M=%lld CPL=%d (c=%d holds the rows)", C, M, s.CPL, c);
-                }
-                if (M > 256 && rows_per_round(C, base, 32, cus) > M)
-                    CHECK(s.CPL == base, "quant C=%d M=%lld cus=%lld CPL=%d", C, M, cus, s.CPL);
+                // two chunks per lane while a round at two holds every row, else three
+                const RowShapeRt s2 = shape_at(C, 2), s3 = shape_at(C, 3);
+                if (rows_per_round(C, 2, 32, cus) >= M)
+                    CHECK(s.NT == s2.NT && s.CPL == s2.CPL, "quant C=%d M=%lld cus=%lld", C, M, cus);
+                else
+                    CHECK(s.NT == s3.NT && s.CPL == s3.CPL, "quant C=%d M=%lld cus=%lld", C, M, cus);
                 ++shapes;
             }
             for (long long cus : cuss)
@@ -137,16 +129,15 @@ int main()
     expect(norm_row_shape(1025, 1000, false, true, 256), 384, 3, 1, "width 8200, 1000 rows, MXFP8 + copy");
     // the standalone per-token quantiser at the sizes it was measured on
     expect(quant_row_shape(1024, 8, 256), 512, 2, 1, "quant width 8192, 8 rows");
-    expect(quant_row_shape(512, 8, 256), 512, 1, 1, "quant width 4096, 8 rows");
-    expect(quant_row_shape(256, 512, 256), 256, 1, 1, "quant width 2048, 512 rows");
-    expect(quant_row_shape(256, 2048, 256), 128, 2, 2, "quant width 2048, 2048 rows (a full round at one)");
-    expect(quant_row_shape(768, 512, 256), 384, 2, 1, "quant width 6144, 512 rows");
-    expect(quant_row_shape(768, 1024, 256), 384, 2, 1, "quant width 6144, 1024 rows");
+    expect(quant_row_shape(1024, 1024, 256), 512, 2, 1, "quant width 8192, 1024 rows (one round at two)");
+    expect(quant_row_shape(1024, 1025, 256), 384, 3, 1, "quant width 8192, 1025 rows");
+    expect(quant_row_shape(256, 8192, 256), 128, 2, 2, "quant width 2048, 8192 rows");
+    expect(quant_row_shape(256, 8193, 256), 128, 2, 2, "quant width 2048, 8193 rows (three collapses to two)");
     expect(quant_row_shape(768, 2048, 256), 256, 3, 1, "quant width 6144, 2048 rows");
-    expect(quant_row_shape(512, 4096, 256), 128, 4, 2, "quant width 4096, 4096 rows");
-    expect(quant_row_shape(1024, 8192, 256), 256, 4, 1, "quant width 8192, 8192 rows (no round holds them)");
-    expect(quant_row_shape(384, 1100, 256), 384, 1, 1, "quant width 3072, 1100 rows");
-    expect(quant_row_shape(1024, 1100, 256), 384, 3, 1, "quant width 8192, 1100 rows");
+    expect(quant_row_shape(32, 5, 256), 64, 1, 4, "quant width 256, 5 rows (one chunk per lane)");
+    expect(quant_row_shape(4096, 8, 256), 1024, 4, 1, "quant width 32768 (four chunks per lane)");
+    expect(quant_row_shape(384, 1100, 256), 192, 2, 1, "quant width 3072, 1100 rows");
+    expect(quant_row_shape(2560, 1100, 256), 896, 3, 1, "quant width 20480, 1100 rows");
     // rows per round: 256 CUs x whole rows in 32 wavefront slots (28 at four chunks per lane)
     CHECK(norm_rows_per_round(768, 1, 256) == 512, "rows per round %lld", (long long)norm_rows_per_round(768, 1, 256));
     CHECK(norm_rows_per_round(768, 2, 256) == 1280, "rows per round %lld", (long long)norm_rows_per_round(768, 2, 256));

@@ -501,11 +501,12 @@ def test_fp8_quant_mx_every_fp16_value_under_every_block_exponent():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("n", [3072, 6144, 8192, 20480, 32768])
+@pytest.mark.parametrize("n", [256, 3072, 8192, 20480, 32768])
 def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
     """The standalone per-token quantiser at 1100 rows, where its row shape
-    takes one chunk per lane at width 3072 (one round holds every row), two
-    at 6144, three at 8192 and four at 20480 and 32768: bit-exact."""
+    takes one chunk per lane at width 256 (64 lanes, four rows per block),
+    two at 3072, three at 8192 and 20480 (a round at two holds fewer rows)
+    and four at 32768: bit-exact."""
     rng = np.random.default_rng(11)
     M = 1100
     x = rng.standard_normal((M, n)) * 2.0 ** rng.integers(-8, 8, (M, 1))
@@ -526,9 +527,9 @@ def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
 
 def test_fp8_quant_per_token_rows_independent_of_shape():
     """The standalone per-token quantiser's row shape follows the row count
-    (width 8192: two chunks per lane at 8 rows, one at 300, three at 1100,
-    four at 2048): the first 8 rows come out bit-identical from every launch, and
-    equal to the oracle's."""
+    (width 8192: two chunks per lane up to 1024 rows, three above): the
+    first 8 rows come out bit-identical from every launch, and equal to the
+    oracle's."""
     rng = np.random.default_rng(23)
     n = 8192
     xh = inputs.to_bits(rng.standard_normal((2048, n)) * 2.0 ** rng.integers(-8, 8, (2048, 1)), "bf16")
