@@ -427,6 +427,12 @@ __device__ __forceinline__ uint2 fp32scale_codes8(const float (&u)[8], const Fp3
 // non-temporal forms (measured faster on every workload here, e.g. the
 // hidden-6144 MXFP8 norm at M = 16384 from 5.5 to 5.8 TB/s).  The norm
 // weight, re-read by every row, uses the ordinary cached load.
+// Wait until every vector memory operation the wavefront has issued is
+// complete: s_waitcnt vmcnt(0), with the expcnt (7) and lgkmcnt (15) fields
+// at their maxima so that they do not wait (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 

@@ -128,6 +128,16 @@ norm_quant_kernel(const NormArgs a)
                     rv[k] = ldg_stream(a.res_in + rrow + lc[k] * 16);
             }
         }
+        // Every load of the row is needed before the first store, so wait for
+        // them all here, before any branch.  Left to itself the compiler cannot
+        // tell at the joins below which loads a wavefront issued, and waits on
+        // the memory counter after the residual store, that is for the store
+        // (headline 146.8 -> 146.3 us, the 1x128 norm at 4096 rows 22.1 ->
+        // 21.6 us, its fp32-direct form 23.2 -> 21.9 us; launches of a few
+        // rows 0.01-0.04 us slower).  The multi-chunk path below keeps the
+        // compiler's per-slot waits: the same early wait there was slower
+        // (width 6144 at 1024 rows 11.2 -> 12.1 us).
+        wait_loads();
 
         // ---- residual add (h = round_dt(x + r), stored), sum of squares
         float h[CPL][8];
