@@ -497,6 +497,11 @@ def run_sweep():
     rec("C5b", "SiLU-and-mul + 1x128, I=3072",
         lambda k: SiluCase(16384, 3072, seed=1, std=3.0, mode="b128", sets=k), 16384,
         silu_bytes(16384, 3072, mode="b128"))
+    # the standalone per-token quantiser (the separate quant of a per-token chain)
+    for M in (8, 1024, 4096):
+        rec("f1", "standalone per-token quant of a bf16 [M, 8192]",
+            lambda k, M=M: QuantCase(M, 8192, seed=0, std=3.0, mode="pt", sets=k), M,
+            M * (3 * 8192 + 4), hot=M <= 64)
     return out
 
 
