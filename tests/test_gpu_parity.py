@@ -525,6 +525,38 @@ def test_fp8_quant_per_token_bandwidth_shapes(dtype, n):
     assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint32), s.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype,n,M", [
+    ("bf16", 256, 7),      # one chunk per lane, 64 lanes, four rows per block (a ragged block)
+    ("bf16", 8192, 300),   # two chunks per lane
+    ("fp16", 8192, 1100),  # three
+    ("fp32", 8192, 1100),  # three, fp32 input (two loads per chunk)
+    ("bf16", 32768, 5),    # four
+])
+def test_fp8_quant_per_token_strided_rows(dtype, n, M):
+    """The per-token quantiser on a column slice of a wider buffer (row
+    stride above the row): every lane loads without a branch, lanes past
+    the row or past the last row from an in-bounds chunk of the last row,
+    so the row stride enters every address.  Bit-exact against the oracle
+    on the slice's contiguous copy."""
+    print(f"case strided per-token quant {dtype} n={n} M={M}", flush=True)
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal((M, n + 64)) * 2.0 ** rng.integers(-8, 8, (M, 1))
+    x[:, 16 + n:] = 1e30 if dtype == "fp32" else 6e4  # past the slice: must not enter any max
+    if dtype == "fp32":
+        xh = x.astype(np.float32)
+        xt = torch.from_numpy(xh).cuda()
+        odt = orc.FP32
+    else:
+        xh = inputs.to_bits(x, dtype)
+        xt = dev16(xh, dtype)
+        odt = ORC_DT[dtype]
+    qa = afq.fp8_quant(xt[:, 16:16 + n], afq.PER_TOKEN)
+    torch.cuda.synchronize()
+    q, sc = orc.quant(np.ascontiguousarray(xh[:, 16:16 + n]), odt, afq.PER_TOKEN, threads=8)
+    assert np.array_equal(host8(qa.values), q)
+    assert np.array_equal(scales_u8_or_f32(qa.scales).view(np.uint32), sc.view(np.uint32))
+
+
 def test_fp8_quant_per_token_rows_independent_of_shape():
     """The standalone per-token quantiser's row shape follows the row count
     (width 8192: two chunks per lane up to 1024 rows, three above): the
