@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     silu_mul_quant(gate_up, mode, ...)             SiLU-and-mul + quant
     swiglu_oai_quant(gate_up, alpha, beta, limit)  clamped SwiGLU + MXFP8
     fp8_quant(x, mode, ...)                        standalone row-wise quant
+and prepare(entry, *args, **kwargs): the arguments of one launch checked and
+marshalled once, for eager loops that launch on the same buffers again.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ import torch  # loaded first: the library then binds to torch's HIP runtime
 __all__ = [
     "MXFP8", "BLOCK128", "PER_TOKEN", "STANDARD", "GEMMA",
     "QIN_DEFAULT", "QIN_FP32", "QIN_BF16",
-    "QuantizedActivation", "AfqError",
+    "QuantizedActivation", "AfqError", "PreparedLaunch", "prepare",
     "fused_add_rmsnorm_quant", "silu_mul_quant", "swiglu_oai_quant", "fp8_quant",
     "abi_version", "status_string", "library_path", "load",
 ]
@@ -253,14 +255,55 @@ def _alloc_out(mode, M, cols, device, normed_dtype, want, out, quantize=True):
     return values, scales, normed
 
 
-def _launch(fn, desc, stream, device: torch.device) -> int:
-    """Call an entry point with the tensors' device current (HIP launches
-    on the current device)."""
-    arg = ctypes.c_void_p(_stream(stream, device))
-    if device.index is not None and device.index != torch.cuda.current_device():
-        with torch.cuda.device(device):
-            return fn(ctypes.byref(desc), arg)
-    return fn(ctypes.byref(desc), arg)
+class PreparedLaunch:
+    """One launch whose arguments were checked and marshalled into its C
+    descriptor once.  Calling it enqueues the same launch again -- same input
+    and output buffers, on the given stream (default: torch's current stream
+    on the buffers' device) -- and returns the same result object, whose
+    tensors the launch has overwritten.  It holds references to every buffer
+    the descriptor points to; the caller must not resize them or change
+    their storage (their contents may change freely between calls: the
+    launch reads them when it runs)."""
+
+    __slots__ = ("_fn", "_desc", "_ref", "_device", "_index", "result", "_keep", "_what")
+
+    def __init__(self, fn, desc, device: torch.device, result, keep, what: str):
+        self._fn, self._desc, self._device = fn, desc, device
+        self._ref = ctypes.byref(desc)
+        self._index = device.index
+        self.result, self._keep, self._what = result, keep, what
+
+    def __call__(self, stream=None):
+        arg = ctypes.c_void_p(_stream(stream, self._device))
+        if self._index is not None and self._index != torch.cuda.current_device():
+            with torch.cuda.device(self._device):
+                st = self._fn(self._ref, arg)
+        else:
+            st = self._fn(self._ref, arg)
+        if st != 0:
+            raise AfqError(st, self._what)
+        return self.result
+
+
+def _finish(fn, desc, stream, device: torch.device, result, keep, what: str, defer: bool):
+    """Launch now (returning the result), or hand back the prepared launch."""
+    call = PreparedLaunch(fn, desc, device, result, keep, what)
+    if defer:
+        return call
+    call(stream)
+    return result
+
+
+def prepare(entry, *args, **kwargs) -> PreparedLaunch:
+    """Check and marshal the arguments of one call of `entry` (one of
+    fused_add_rmsnorm_quant, silu_mul_quant, swiglu_oai_quant, fp8_quant)
+    without launching; the returned PreparedLaunch launches it.  Outputs not
+    passed in `out` are allocated here, once, and reused by every call."""
+    if entry not in (fused_add_rmsnorm_quant, silu_mul_quant, swiglu_oai_quant, fp8_quant):
+        raise ValueError("prepare takes one of the library's entry points")
+    if "stream" in kwargs:
+        raise ValueError("pass the stream to the prepared launch, not to prepare")
+    return entry(*args, _defer=True, **kwargs)
 
 
 # ------------------------------------------------------------- entry points
@@ -279,6 +322,7 @@ def fused_add_rmsnorm_quant(
     quantize: bool = True,
     out=None,
     stream=None,
+    _defer: bool = False,
 ):
     """Residual add + RMSNorm + FP8 quantisation in one launch.
 
@@ -347,10 +391,10 @@ def fused_add_rmsnorm_quant(
         results[0].residual = residual_out
     elif residual_out is not None:
         raise ValueError("residual_out needs a residual")
-    st = _launch(lib.fused_add_rmsnorm_quant, d, stream, device)
-    if st != 0:
-        raise AfqError(st, "fused_add_rmsnorm_quant")
-    return results[0] if len(results) == 1 else results
+    keep = (xs, ws, residual)
+    return _finish(lib.fused_add_rmsnorm_quant, d, stream, device,
+                   results[0] if len(results) == 1 else results, keep, "fused_add_rmsnorm_quant",
+                   _defer)
 
 
 def _act_desc(gate_up, mode, want_act, quant_input, quantize, out):
@@ -374,7 +418,7 @@ def _act_desc(gate_up, mode, want_act, quant_input, quantize, out):
 
 def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
                    quant_input: int = QIN_DEFAULT, quantize: bool = True, out=None,
-                   stream=None) -> QuantizedActivation:
+                   stream=None, _defer: bool = False) -> QuantizedActivation:
     """SiLU-and-mul of a bf16 [M, 2I] row ([gate | up]) + FP8 quantisation.
 
     MXFP8 quantises the fp32 activation; BLOCK128 rounds silu and the product
@@ -387,15 +431,14 @@ def silu_mul_quant(gate_up: torch.Tensor, mode=MXFP8, *, want_act: bool = False,
     lib = load()
     mode = _mode(mode)
     d, qa = _act_desc(gate_up, mode, want_act, quant_input, quantize, out)
-    st = _launch(lib.silu_mul_quant, d, stream, gate_up.device)
-    if st != 0:
-        raise AfqError(st, "silu_mul_quant")
-    return qa
+    return _finish(lib.silu_mul_quant, d, stream, gate_up.device, qa, gate_up, "silu_mul_quant",
+                   _defer)
 
 
 def swiglu_oai_quant(gate_up: torch.Tensor, alpha: float, beta: float, limit: float, *,
                      want_act: bool = False, quant_input: int = QIN_DEFAULT,
-                     quantize: bool = True, out=None, stream=None) -> QuantizedActivation:
+                     quantize: bool = True, out=None, stream=None,
+                     _defer: bool = False) -> QuantizedActivation:
     """Clamped SwiGLU of a bf16 [M, 2I] row ([gate | up]) + MXFP8:
     a = fp32(glu) * fp32(clamp(up, +-limit) + beta), glu = gc * logistic(alpha
     * gc), gc = min(gate, limit), quantised in fp32.  quant_input=QIN_BF16
@@ -405,13 +448,12 @@ def swiglu_oai_quant(gate_up: torch.Tensor, alpha: float, beta: float, limit: fl
     d, qa = _act_desc(gate_up, MXFP8, want_act, quant_input, quantize, out)
     sd = _SwigluDesc()
     sd.act, sd.alpha, sd.beta, sd.limit = d, float(alpha), float(beta), float(limit)
-    st = _launch(lib.swiglu_oai_quant, sd, stream, gate_up.device)
-    if st != 0:
-        raise AfqError(st, "swiglu_oai_quant")
-    return qa
+    return _finish(lib.swiglu_oai_quant, sd, stream, gate_up.device, qa, gate_up,
+                   "swiglu_oai_quant", _defer)
 
 
-def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> QuantizedActivation:
+def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None,
+              _defer: bool = False) -> QuantizedActivation:
     """Standalone row-wise FP8 quantisation of a bf16 / fp16 / fp32 [M, cols]."""
     lib = load()
     mode = _mode(mode)
@@ -426,7 +468,6 @@ def fp8_quant(x: torch.Tensor, mode=MXFP8, *, out=None, stream=None) -> Quantize
     d.M, d.cols, d.x, d.x_row_stride = M, cols, x.data_ptr(), x.stride(0)
     d.dtype, d.mode = _DTYPE_TAG[x.dtype], mode
     d.out.values, d.out.scales, d.out.normed = _ptr(values), _ptr(scales), None
-    st = _launch(lib.fp8_quant, d, stream, x.device)
-    if st != 0:
-        raise AfqError(st, "fp8_quant")
-    return QuantizedActivation(values, scales, None, None, mode, x.dtype, (M, cols))
+    return _finish(lib.fp8_quant, d, stream, x.device,
+                   QuantizedActivation(values, scales, None, None, mode, x.dtype, (M, cols)), x,
+                   "fp8_quant", _defer)

@@ -3,12 +3,19 @@
 Agreement required (the contract of the library):
   * bf16 / fp16 outputs: at most 1 unit in the last place apart (distance in
     the monotone integer order of the encoding), bit-exact where stated;
-  * scales: exact in at least 99.9 % of groups (at least all but one in small
-    tests); the rest off by one E8M0 step, one fp32 ulp, or -- for fp32
-    scales -- explained by a one-ulp difference of the rounded activation
-    (checked separately by re-quantising the GPU's own rounded row);
+  * scales: exact in at least 99.9 % of groups, that is at most
+    floor(n / 1000) inexact among the n groups a check covers, unless the
+    test states its own budget.  Every inexact scale is listed and must be
+    explained:
+      - E8M0 bytes: one exponent step apart;
+      - fp32 scales: one fp32 ulp apart, or the reading R14 case: the group's
+        largest activation rounded to the neighbouring dtype value on the GPU,
+        so the scale is fl32(A'/448) with A' the next or previous dtype value
+        of the oracle's group amax A (the oracle's rounded activation is
+        passed in to decide this; without it only the one-ulp case counts);
   * e4m3 codes: equal, or one code apart in at most 0.1 % of elements
-    (at most one element in small tests).  0x00 and 0x80 are both zero.
+    (floor(n / 1000), unless the test states its budget).  0x00 and 0x80 are
+    both zero.
 """
 from __future__ import annotations
 
@@ -36,7 +43,16 @@ def ord32(f: np.ndarray) -> np.ndarray:
 
 
 def budget(n: int, frac: float = 1e-3) -> int:
-    return max(1, math.floor(frac * n))
+    """Inexact groups (or one-apart codes) the contract admits among n."""
+    return math.floor(frac * n)
+
+
+def decode16(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """uint16 bit patterns of bf16 / fp16 -> float32 values (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == "bf16":
+        return (b.astype(np.uint32) << 16).view(np.float32)
+    return b.view(np.float16).astype(np.float32)
 
 
 def check_dtype16(gpu, ref, name, max_ulp=1, exact=False):
@@ -49,26 +65,76 @@ def check_dtype16(gpu, ref, name, max_ulp=1, exact=False):
     return int((d != 0).sum())
 
 
-def check_codes(gpu, ref, name):
+def check_codes(gpu, ref, name, allowed=None):
+    """Codes equal, or one apart in at most `allowed` elements (default
+    floor(n / 1000)).  Returns the number one apart."""
     d = np.abs(ord8(gpu) - ord8(ref))
     n1 = int((d == 1).sum())
     assert d.max(initial=0) <= 1, f"{name}: code distance {d.max()} at {np.argwhere(d > 1)[:5].tolist()}"
-    assert n1 <= budget(d.size), f"{name}: {n1} of {d.size} codes one step apart"
+    lim = budget(d.size) if allowed is None else allowed
+    assert n1 <= lim, f"{name}: {n1} of {d.size} codes one step apart (budget {lim})"
     return n1
 
 
-def check_scales(gpu, ref, mode, name):
-    """mode 0: uint8 E8M0 bytes; else fp32."""
+def _r14_scales(u_bits: np.ndarray, dtype: str, ngroups: int):
+    """For each group of the oracle's rounded activation u [M, cols]: the
+    fp32 scales fl32(A'/448) of the amax A moved one dtype value down and up
+    (numpy float32 division is the IEEE one).  Returns two [M, ngroups]
+    float32 arrays (NaN where the neighbour does not exist)."""
+    u = np.ascontiguousarray(u_bits, dtype=np.uint16)
+    M, cols = u.shape
+    mag = (u & 0x7FFF).reshape(M, ngroups, cols // ngroups)
+    a = mag.max(axis=2).astype(np.int64)                        # |A| bit pattern (orders like |A|)
+    top = 0x7F7F if dtype == "bf16" else 0x7BFF                 # largest finite magnitude
+    lo = np.where(a > 0, a - 1, 0).astype(np.uint16)
+    hi = np.minimum(a + 1, top).astype(np.uint16)
+    s_lo = decode16(lo, dtype) / np.float32(448.0)
+    s_hi = decode16(hi, dtype) / np.float32(448.0)
+    s_lo[a == 0] = np.nan
+    s_hi[a >= top] = np.nan
+    return s_lo.astype(np.float32), s_hi.astype(np.float32)
+
+
+def check_scales(gpu, ref, mode, name, *, u=None, dtype=None, allowed=None):
+    """mode 0: uint8 E8M0 bytes; else fp32 scales [M, groups].
+
+    Every inexact scale is explained (see the module docstring) and listed
+    in the returned report; at most `allowed` (default floor(n / 1000)) may
+    be inexact.  `u` / `dtype`: the oracle's rounded activation [M, cols]
+    (bit patterns) and its dtype, to recognise the R14 case.
+    Returns (number inexact, list of (flat index, explanation))."""
+    listed = []
     if mode == 0:
         d = np.abs(np.asarray(gpu, np.int64) - np.asarray(ref, np.int64))
-        assert d.max(initial=0) <= 1, f"{name}: E8M0 off by {d.max()}"
+        assert d.max(initial=0) <= 1, f"{name}: E8M0 off by {d.max()} at {np.argwhere(d > 1)[:5].tolist()}"
+        for i in np.flatnonzero(d):
+            listed.append((int(i), "one E8M0 step"))
+        n = d.size
     else:
-        gb = np.ascontiguousarray(gpu, np.float32).view(np.uint32)
-        rb = np.ascontiguousarray(ref, np.float32).view(np.uint32)
-        d = (gb != rb).astype(np.int64)
-    nbad = int((d != 0).sum())
-    assert nbad <= budget(d.size), f"{name}: {nbad} of {d.size} scales inexact"
-    return nbad
+        g = np.ascontiguousarray(gpu, np.float32)
+        r = np.ascontiguousarray(ref, np.float32)
+        n = r.size
+        bad = np.flatnonzero(g.view(np.uint32).ravel() != r.view(np.uint32).ravel())
+        if bad.size:
+            dist = np.abs(ord32(g).ravel() - ord32(r).ravel())
+            s_lo = s_hi = None
+            if u is not None:
+                groups = r.reshape(r.shape[0], -1).shape[1]
+                s_lo, s_hi = _r14_scales(u, dtype, groups)
+                s_lo, s_hi = s_lo.ravel().view(np.uint32), s_hi.ravel().view(np.uint32)
+            gb = g.view(np.uint32).ravel()
+            for i in bad:
+                if dist[i] == 1:
+                    listed.append((int(i), "one fp32 ulp"))
+                elif s_lo is not None and gb[i] in (s_lo[i], s_hi[i]):
+                    listed.append((int(i), "R14: amax one dtype value away"))
+                else:
+                    raise AssertionError(
+                        f"{name}: scale {i} is {float(g.ravel()[i])!r}, oracle {float(r.ravel()[i])!r} "
+                        f"({dist[i]} fp32 ulps apart, not explained by a one-ulp amax flip)")
+    lim = budget(n) if allowed is None else allowed
+    assert len(listed) <= lim, f"{name}: {len(listed)} of {n} scales inexact (budget {lim}): {listed[:10]}"
+    return len(listed), listed
 
 
 def scales_u8_or_f32(t):

@@ -1,0 +1,143 @@
+// afq_probe.hip -- test-only probe kernels (not part of libafq.so).
+//
+// Each kernel applies one of the library's device primitives (from
+// afq_device.hpp, the header the product kernels use) element-wise, so that
+// the tests can compare the primitive with IEEE arithmetic and with the
+// oracle's roundings on the host, over exhaustive input sets:
+//   afqp_scale     fp32_scale(amax): the stored scale s, the reciprocal r
+//                  and the fast-path flag
+//   afqp_quotient  the quotient a quantiser forms for u under amax's scale
+//                  (quotient_fast on the fast path, IEEE division otherwise)
+//   afqp_cvt8_e4m3 cvt8_e4m3 on 8 values at a time (v_cvt_pk_fp8_f32, both
+//                  word halves), no clamp
+//   afqp_e4m3_range the same on every fp32 bit pattern base .. base + n - 1,
+//                  generated in the kernel
+//   afqp_pack_bf16 pack8<bf16> on 8 values at a time (v_cvt_pk_bf16_f32)
+//
+// Every kernel is guarded by its element count; the host wrappers reject
+// counts above 2^31, counts that are not a multiple of 8 where 8 values go
+// to one lane, and buffers not 16-byte aligned, before launching.
+#include "afq_device.hpp"
+
+using namespace afq;
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ void __launch_bounds__(kBlock) k_scale(const float *amax, float *s, float *r, uint8_t *fast, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    const Fp32Scale sc = fp32_scale(amax[i]);
+    s[i] = sc.s;
+    r[i] = sc.r;
+    fast[i] = sc.fast ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(kBlock) k_quotient(const float *u, const float *amax, float *q, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    const Fp32Scale sc = fp32_scale(amax[i]);
+    q[i] = sc.fast ? quotient_fast(u[i], sc) : u[i] / sc.s;
+}
+
+__global__ void __launch_bounds__(kBlock) k_cvt8(const float *v, uint8_t *codes, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n8) return;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = v[i * 8 + k];
+    *reinterpret_cast<uint2 *>(codes + i * 8) = cvt8_e4m3(x);
+}
+
+__global__ void __launch_bounds__(kBlock) k_e4m3_range(uint32_t base, uint8_t *codes, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n8) return;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(base + (uint32_t)(i * 8 + k));
+    *reinterpret_cast<uint2 *>(codes + i * 8) = cvt8_e4m3(x);
+}
+
+__global__ void __launch_bounds__(kBlock) k_pack_bf16(const float *v, uint16_t *out, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n8) return;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = v[i * 8 + k];
+    *reinterpret_cast<uint4 *>(out + i * 8) = pack8<kBF16>(x);
+}
+
+// threads needed for n work items, or -1 when n is out of range
+int64_t grid_for(int64_t n)
+{
+    if (n < 0 || n > ((int64_t)1 << 31)) return -1;
+    return (n + kBlock - 1) / kBlock;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+} // namespace
+
+extern "C" {
+
+// All pointers are device pointers; n counts elements.  Returns 0, -1 for a
+// rejected count, or the HIP error of the launch.
+int afqp_scale(const float *amax, float *s, float *r, uint8_t *fast, int64_t n, void *stream)
+{
+    const int64_t g = grid_for(n);
+    if (g < 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_scale, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, amax, s, r, fast, n);
+    return (int)hipGetLastError();
+}
+
+int afqp_quotient(const float *u, const float *amax, float *q, int64_t n, void *stream)
+{
+    const int64_t g = grid_for(n);
+    if (g < 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_quotient, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, u, amax, q, n);
+    return (int)hipGetLastError();
+}
+
+// n must be a multiple of 8; codes holds n bytes
+int afqp_cvt8_e4m3(const float *v, uint8_t *codes, int64_t n, void *stream)
+{
+    if (n % 8 || !aligned16(v) || !aligned16(codes)) return -1;
+    const int64_t g = grid_for(n / 8);
+    if (g < 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_cvt8, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, v, codes, n / 8);
+    return (int)hipGetLastError();
+}
+
+// codes[i] = e4m3 of the fp32 with bit pattern base + i, i < n; n a multiple
+// of 8 and base + n <= 2^32
+int afqp_e4m3_range(uint32_t base, uint8_t *codes, int64_t n, void *stream)
+{
+    if (n % 8 || (int64_t)base + n > ((int64_t)1 << 32) || !aligned16(codes)) return -1;
+    const int64_t g = grid_for(n / 8);
+    if (g < 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_e4m3_range, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, base, codes, n / 8);
+    return (int)hipGetLastError();
+}
+
+// n must be a multiple of 8; out holds n bf16 bit patterns
+int afqp_pack_bf16(const float *v, uint16_t *out, int64_t n, void *stream)
+{
+    if (n % 8 || !aligned16(v) || !aligned16(out)) return -1;
+    const int64_t g = grid_for(n / 8);
+    if (g < 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_pack_bf16, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, v, out, n / 8);
+    return (int)hipGetLastError();
+}
+
+} // extern "C"

@@ -49,3 +49,14 @@ def test_committed_traffic_record_uses_the_same_bytes():
     assert rec["algorithmic_bytes_per_launch"] == bench.norm_bytes(16384, 6144)
     ratio = rec["traffic_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
     assert 0.99 < ratio < 1.05, ratio
+
+
+def test_copy_only_bytes():
+    # the copy-only launches (the in-repo memory-pattern figures): the norm
+    # reads x and r and writes h and the rounded copy; the weight once
+    assert bench.norm_bytes(4096, 6144, quant=False) == 4096 * 4 * 2 * 6144 + 2 * 6144
+    assert bench.norm_bytes(4096, 4096, mode="b128", quant=False) == 4096 * 4 * 2 * 4096 + 2 * 4096
+    # SiLU-and-mul: [gate | up] in, the bf16 activation out
+    assert bench.silu_bytes(16384, 3072, quant=False) == 16384 * (2 * 2 * 3072 + 2 * 3072)
+    # two segments without residual: x in, the copy out, both weights once
+    assert bench.two_seg_bytes(8192, quant=False) == 8192 * 2 * 2 * 2048 + 2 * 2048

@@ -1,0 +1,214 @@
+"""The gfx950 instructions and fast arithmetic the kernels rely on, checked
+on the GPU over exhaustive input sets (the probe library in tests/probe
+applies the library's own device primitives element-wise):
+
+  * the fp32 scale amax/448 of the 1x128 and per-token quantisers: on the
+    fast path a product with RN(1/448) plus one correction, and RN(1/s) as
+    the hardware reciprocal plus one Newton step.  Both must equal the IEEE
+    divisions (numpy float32 on the host) for every fp32 mantissa at every
+    exponent; below amax = 2^-116 the kernels take the IEEE divisions;
+  * the corrected quotient u/s (correctly rounded, Markstein) for u = +-amax
+    (quotients at 448 and at most one ulp beyond it) and random u, every
+    amax mantissa at boundary and middle exponents;
+  * v_cvt_pk_fp8_f32, unclamped, on every fp32 in [448, 464] of either sign
+    (what the fast path can hand it beyond 448 is at most 448(1 + 2^-23))
+    and on every fp32 in [2^-10, 464) of either sign, against the oracle's
+    e4m3 rounding;
+  * v_cvt_pk_bf16_f32 on every bf16 neighbourhood of the fp32 line: each of
+    the 2^16 upper halves with the lower halves that decide round to nearest
+    even (0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF and two random), against the
+    oracle's bf16 rounding.
+"""
+import concurrent.futures
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from tests._gpu import HOST_THREADS
+
+pytestmark = pytest.mark.gpu
+
+PROBE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probe", "libafq_probe.so")
+
+
+def _probe():
+    if not os.path.exists(PROBE):
+        raise FileNotFoundError(f"{PROBE} is missing: build it with `python -m tests.probe.build`")
+    L = ctypes.CDLL(PROBE)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    L.afqp_scale.argtypes = [P, P, P, P, I64, P]
+    L.afqp_quotient.argtypes = [P, P, P, I64, P]
+    L.afqp_cvt8_e4m3.argtypes = [P, P, I64, P]
+    L.afqp_e4m3_range.argtypes = [ctypes.c_uint32, P, I64, P]
+    L.afqp_pack_bf16.argtypes = [P, P, I64, P]
+    for f in (L.afqp_scale, L.afqp_quotient, L.afqp_cvt8_e4m3, L.afqp_e4m3_range, L.afqp_pack_bf16):
+        f.restype = ctypes.c_int
+    return L
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _binade(E: int) -> np.ndarray:
+    """Every fp32 of exponent field E, ascending, as float32."""
+    return ((np.uint32(E) << np.uint32(23)) | np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+
+
+def _gpu_scale(L, a: np.ndarray):
+    at = torch.from_numpy(a).cuda()
+    s, r = torch.empty_like(at), torch.empty_like(at)
+    f = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+    rc = L.afqp_scale(at.data_ptr(), s.data_ptr(), r.data_ptr(), f.data_ptr(), a.size, _stream())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), r.cpu().numpy(), f.cpu().numpy().astype(bool)
+
+
+def test_fp32_scale_and_reciprocal_every_mantissa_every_exponent():
+    """s = amax/448 and 1/s against IEEE float32 division for all 2^23
+    mantissas of every exponent field 0..254 (2.1 G amax values): s
+    bit-exact everywhere, 1/s bit-exact wherever the quantiser uses it (the
+    fast flag), and the fast flag set exactly where s is normal and 1/s
+    finite, which includes every amax >= 2^-116."""
+    L = _probe()
+    four48, one = np.float32(448.0), np.float32(1.0)
+    fast_seen = 0
+    for E0 in range(0, 255, 8):
+        Es = list(range(E0, min(E0 + 8, 255)))
+        print(f"case fp32 scale exponent fields {Es[0]}..{Es[-1]}", flush=True)
+        a = np.concatenate([_binade(E) for E in Es])
+        s, r, fast = _gpu_scale(L, a)
+        with np.errstate(divide="ignore", over="ignore"):
+            s_ref = a / four48
+            r_ref = one / s_ref
+        bad = np.flatnonzero(s.view(np.uint32) != s_ref.view(np.uint32))
+        assert bad.size == 0, [(float(a[i]), float(s[i]), float(s_ref[i])) for i in bad[:5]]
+        fast_ref = (s_ref >= np.float32(2.0 ** -126)) & (r_ref < np.float32(2.0 ** 127))
+        assert np.array_equal(fast, fast_ref), np.flatnonzero(fast != fast_ref)[:5]
+        assert bool(fast[a >= np.float32(2.0 ** -116)].all())
+        bad = np.flatnonzero(fast & (r.view(np.uint32) != r_ref.view(np.uint32)))
+        assert bad.size == 0, [(float(a[i]), float(r[i]), float(r_ref[i])) for i in bad[:5]]
+        fast_seen += int(fast.sum())
+    assert fast_seen > 0
+
+
+@pytest.mark.parametrize("E", [11, 12, 13, 20, 100, 127, 128, 200, 253, 254])
+def test_fp32_quotient_correctly_rounded(E):
+    """The quantiser's quotient u/s for every amax mantissa of exponent field
+    E (amax >= 2^-116 from field 11: the fast path), with u = amax, -amax
+    (quotients at 448 or one ulp beside it) and a random |u| <= amax:
+    bit-exact against IEEE float32 division, and some quotients land in
+    (448, 448(1 + 2^-23)]."""
+    L = _probe()
+    a = _binade(E)
+    rng = np.random.default_rng(E)
+    frac = rng.random(a.size).astype(np.float32)
+    u_rand = (a * frac) * np.where(rng.random(a.size) < 0.5, np.float32(-1), np.float32(1))
+    u = np.concatenate([a, -a, u_rand.astype(np.float32)])
+    aa = np.concatenate([a, a, a])
+    ut, at = torch.from_numpy(u).cuda(), torch.from_numpy(aa).cuda()
+    q = torch.empty_like(ut)
+    rc = L.afqp_quotient(ut.data_ptr(), at.data_ptr(), q.data_ptr(), u.size, _stream())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    q = q.cpu().numpy()
+    q_ref = u / (aa / np.float32(448.0))
+    bad = np.flatnonzero(q.view(np.uint32) != q_ref.view(np.uint32))
+    assert bad.size == 0, [(float(u[i]), float(aa[i]), float(q[i]), float(q_ref[i])) for i in bad[:5]]
+    above = int((np.abs(q_ref) > np.float32(448.0)).sum())
+    assert above > 0 and float(np.abs(q_ref).max()) == float(np.nextafter(np.float32(448), np.float32(512)))
+    print(f"[sweep] quotient E={E}: {u.size} quotients, {above} above 448", flush=True)
+
+
+def _oracle_e4m3(bits: np.ndarray) -> np.ndarray:
+    """The oracle's e4m3 rounding of fp32 bit patterns, over host threads."""
+    out = np.empty(bits.size, np.uint8)
+    chunk = 1 << 22
+
+    def run(i):
+        v = bits[i:i + chunk].view(np.float32).astype(np.float64)
+        out[i:i + chunk] = orc.round_e4m3(v)
+
+    with concurrent.futures.ThreadPoolExecutor(HOST_THREADS) as ex:
+        list(ex.map(run, range(0, bits.size, chunk)))
+    return out
+
+
+def _gpu_e4m3_range(L, base: int, n: int) -> np.ndarray:
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    rc = L.afqp_e4m3_range(base, codes.data_ptr(), n, _stream())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    return codes.cpu().numpy()
+
+
+@pytest.mark.parametrize("sign", [0, 1])
+def test_cvt_fp8_unclamped_448_to_464(sign):
+    """v_cvt_pk_fp8_f32 without a clamp on every fp32 from just below 448 to
+    464 inclusive: every one gives +-448 (0x7E / 0xFE), as the oracle's
+    rounding of the clamped value does."""
+    L = _probe()
+    lo = int(np.float32(448.0).view(np.uint32)) - 7
+    hi = int(np.float32(464.0).view(np.uint32))
+    n = hi - lo + 1
+    assert n % 8 == 0
+    base = lo | (sign << 31)
+    got = _gpu_e4m3_range(L, base, n)
+    bits = np.arange(base, base + n, dtype=np.uint64).astype(np.uint32)
+    want = _oracle_e4m3(bits)
+    assert bool((want == (0x7E | (sign << 7))).all())
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(int(bits[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+@pytest.mark.parametrize("sign", [0, 1])
+def test_cvt_fp8_every_fp32_below_464(sign):
+    """v_cvt_pk_fp8_f32 on every fp32 in [2^-10, 464) of one sign (exponent
+    fields 117..135; smaller magnitudes round to zero, covered by the
+    structured test): 159 M values against the oracle's e4m3 rounding."""
+    L = _probe()
+    top = int(np.float32(464.0).view(np.uint32))
+    start = 117 << 23
+    step = 1 << 24
+    for b0 in range(start, top, step):
+        n = min(step, top - b0)
+        base = b0 | (sign << 31)
+        print(f"case e4m3 sweep base {base:#010x} n {n}", flush=True)
+        got = _gpu_e4m3_range(L, base, n)
+        bits = np.arange(base, base + n, dtype=np.uint64).astype(np.uint32)
+        want = _oracle_e4m3(bits)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, [(hex(int(bits[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_cvt_bf16_round_to_nearest_even_classes():
+    """v_cvt_pk_bf16_f32 (the kernels' dtype rounding) on every upper half
+    of a finite fp32 combined with the lower halves that decide round to
+    nearest even -- below, at and above the midpoint, the ends, and two
+    random -- against the oracle's bf16 rounding (overflow to infinity
+    included)."""
+    L = _probe()
+    hi = np.arange(1 << 16, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]
+    rng = np.random.default_rng(5)
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = np.concatenate([(hi << 16) | lw for lw in lows]
+                          + [(hi << 16) | rng.integers(0, 1 << 16, hi.size).astype(np.uint32)
+                             for _ in range(2)])
+    v = bits.view(np.float32)
+    pad = (-v.size) % 8
+    v = np.concatenate([v, np.zeros(pad, np.float32)])
+    vt = torch.from_numpy(v).cuda()
+    out = torch.empty(v.size, dtype=torch.int16, device="cuda")
+    rc = L.afqp_pack_bf16(vt.data_ptr(), out.data_ptr(), v.size, _stream())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)[:bits.size]
+    want = orc.round_bf16(v[:bits.size].astype(np.float64))
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(int(bits[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]

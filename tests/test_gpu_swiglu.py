@@ -47,7 +47,7 @@ def _ref_act(act, gu):
 
 def _check(gpu, ref, name):
     n1 = check_codes(gpu["values"], ref["values"], name)
-    nb = check_scales(gpu["scales"], ref["scales"], 0, name)
+    nb, _ = check_scales(gpu["scales"], ref["scales"], 0, name)
     out = dict(codes_1=n1, scales_bad=nb)
     if gpu["act"] is not None:
         out["act_1ulp"] = check_dtype16(gpu["act"], ref["act"], name + " act")
