@@ -9,10 +9,12 @@
 // 4 consecutive lanes, a 128-element group exactly 16 (one DPP row).
 //
 // Conversions use the gfx950 packed instructions v_cvt_pk_bf16_f32 and
-// v_cvt_pk_fp8_f32 (OCP e4m3fn).  Both round to nearest even; checked
-// against the integer definitions of those roundings on every fp32 input
-// (v_cvt_pk_fp8_f32 on every |v| <= 448, which is all it is given: values
-// are clamped first).
+// v_cvt_pk_fp8_f32 (OCP e4m3fn).  Both round to nearest even, as the GPU
+// tests check against the oracle's roundings: v_cvt_pk_fp8_f32 on every
+// fp32 from 2^-10 (below it everything rounds to zero) to 464 of either
+// sign, which covers all it is given (clamped values, or quotients of at
+// most 448(1+2^-23)); v_cvt_pk_bf16_f32 on every rounding class of every
+// bf16 neighbourhood.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -359,41 +361,49 @@ __device__ __forceinline__ uint2 mx_codes8(const float (&u)[8], float inv_x)
 // fp32 scale s = amax / 448 and the reciprocal used by the quotient below.
 struct Fp32Scale {
     float s;    // stored scale
-    float r;    // RN(1/s) when the fast quotient is valid
-    bool fast;  // s normal and 1/s finite
-    bool zero;  // all-zero group
+    float r;    // RN(1/s), set when fast
+    bool fast;  // fast scale and fast quotient valid (amax >= 2^-83)
+    bool zero;  // s == 0: an all-zero group, or one whose amax / 448
+                // underflows fp32; its codes are all 0x00
 };
-// For amax >= 2^-116 (s and 1/s normal): s = RN(amax/448) as a product
-// with RN(1/448) plus one Markstein correction, and RN(1/s) as the hardware
-// reciprocal plus one Newton correction.  Both equal the IEEE divisions on
-// every fp32 mantissa at every exponent of that range (checked on the GPU
-// over all 2^23 mantissas); smaller amax take the IEEE divisions.
+// Fast path, amax >= 2^-83: s = RN(amax/448) as a product with RN(1/448)
+// plus one Markstein correction, and RN(1/s) as the hardware reciprocal plus
+// one Newton correction.  Both equal the IEEE divisions on every fp32
+// mantissa at every exponent from 2^-116 up (checked on the GPU over all
+// 2^23 mantissas of every exponent field).  The bound 2^-83 is the
+// quotient's: its remainder (below) is exact when it is no finer than the
+// smallest subnormal, which for every quotient of 2^-11 or more (all that
+// decide an e4m3 code) needs s >= 2^-92, i.e. amax >= 448 * 2^-92 ~ 2^-83.2;
+// below that the remainder can round and the corrected quotient miss the
+// correctly rounded one.  Smaller amax take the IEEE divisions.
 __device__ __forceinline__ Fp32Scale fp32_scale(float amax)
 {
     Fp32Scale sc;
-    sc.zero = (amax == 0.0f);
-    if (__builtin_expect(amax >= 0x1p-116f, 1)) {
+    if (__builtin_expect(amax >= 0x1p-83f, 1)) {
         constexpr float kInv448 = 1.0f / 448.0f;
         const float s0 = amax * kInv448;
         sc.s = __builtin_fmaf(__builtin_fmaf(-s0, 448.0f, amax), kInv448, s0);
         const float r0 = __builtin_amdgcn_rcpf(sc.s);
         sc.r = __builtin_fmaf(__builtin_fmaf(-sc.s, r0, 1.0f), r0, r0);
         sc.fast = true;
+        sc.zero = false;
     } else {
         sc.s = amax / 448.0f;      // IEEE division
-        sc.r = 1.0f / sc.s;        // IEEE division, correctly rounded
-        sc.fast = (sc.s >= 0x1p-126f) && (sc.r < 0x1p127f);
+        sc.r = 0.0f;
+        sc.fast = false;
+        sc.zero = (sc.s == 0.0f);
     }
     return sc;
 }
 
 // fp32(u / s), correctly rounded, for a scale with sc.fast set.  With
 // r = RN(1/s), q0 = RN(u r) is within one ulp of u/s, so the remainder
-// q0 s - u is exact under FMA, and one correction step q0 - (q0 s - u) r
-// rounds to the correctly rounded quotient (Markstein's theorem; no
-// overflow since |u/s| <= 448(1+2^-23)).  Taking the remainder as q0 s - u
-// keeps the sign of a zero u (-0 gives -0): for u = -0 the correction is
-// -(+0) r + (-0) = -0.
+// q0 s - u is exact under FMA (no finer than the smallest subnormal for
+// every quotient that can decide a code: amax >= 2^-83), and one correction
+// step q0 - (q0 s - u) r rounds to the correctly rounded quotient
+// (Markstein's theorem; no overflow since |u/s| <= 448(1+2^-23)).  Taking the
+// remainder as q0 s - u keeps the sign of a zero u (-0 gives -0): for u = -0
+// the correction is -(+0) r + (-0) = -0.
 __device__ __forceinline__ float quotient_fast(float u, const Fp32Scale &sc)
 {
     const float q0 = u * sc.r;
@@ -404,10 +414,9 @@ __device__ __forceinline__ float quotient_fast(float u, const Fp32Scale &sc)
 // 8 codes of a chunk under an fp32 scale.  With a fast scale the quotients
 // are at most 448(1+2^-23) in magnitude, which v_cvt_pk_fp8_f32 rounds to
 // 448 exactly as it rounds the clamped value (checked on the GPU over every
-// fp32 in [448, 464] of either sign), so no clamp is applied.  Scales that
-// are subnormal or whose reciprocal overflows (amax below 448 * 2^-126) take
-// the IEEE division and the clamp.  The choice is made once per chunk (it is
-// uniform over a group).
+// fp32 in [448, 464] of either sign), so no clamp is applied.  Other scales
+// take the IEEE division and the clamp; a zero scale gives zero codes.  The
+// choice is made once per chunk (it is uniform over a group).
 __device__ __forceinline__ uint2 fp32scale_codes8(const float (&u)[8], const Fp32Scale &sc)
 {
     float v[8];

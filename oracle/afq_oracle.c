@@ -226,8 +226,10 @@ static void quant_mx_group(const double *u, int g, uint8_t *q, uint8_t *sbyte)
 
 /* Block (1x128) and per-token: fp32 scale s = amax / 448 ([P2]
  * "Modifications": the per-1x128 quant; [P4] "Change": x_scale[m,1]); the
- * code is e4m3 of the fp32 quotient u/s, clamped to +-448.  An all-zero
- * group has s = 0 and codes 0x00. */
+ * code is e4m3 of the fp32 quotient u/s, clamped to +-448.  A group whose
+ * stored scale is 0 -- all zero, or an amax so small (at most 224 * 2^-149)
+ * that amax / 448 underflows fp32 -- has codes 0x00: with s = 0 every
+ * dequantised value is 0, as for the all-zero group. */
 static void quant_fp32scale_group(const double *u, int g, uint8_t *q, float *s_out)
 {
     double amax = 0.0;
@@ -236,7 +238,7 @@ static void quant_fp32scale_group(const double *u, int g, uint8_t *q, float *s_o
     float s = A / 448.0f; /* IEEE fp32 division */
     *s_out = s;
     for (int j = 0; j < g; ++j) {
-        if (A == 0.0f) { q[j] = 0x00; continue; }
+        if (s == 0.0f) { q[j] = 0x00; continue; }
         float t = (float)u[j] / s; /* IEEE fp32 division */
         q[j] = orc_round_e4m3(clamp448((double)t));
     }

@@ -108,7 +108,7 @@ def check_scales(gpu, ref, mode, name, *, u=None, dtype=None, allowed=None):
         d = np.abs(np.asarray(gpu, np.int64) - np.asarray(ref, np.int64))
         assert d.max(initial=0) <= 1, f"{name}: E8M0 off by {d.max()} at {np.argwhere(d > 1)[:5].tolist()}"
         for i in np.flatnonzero(d):
-            listed.append((int(i), "one E8M0 step"))
+            listed.append((int(i), "one E8M0 step"))   # explained further by check_quant
         n = d.size
     else:
         g = np.ascontiguousarray(gpu, np.float32)
@@ -135,6 +135,66 @@ def check_scales(gpu, ref, mode, name, *, u=None, dtype=None, allowed=None):
     lim = budget(n) if allowed is None else allowed
     assert len(listed) <= lim, f"{name}: {len(listed)} of {n} scales inexact (budget {lim}): {listed[:10]}"
     return len(listed), listed
+
+
+def _moved_group_quant(u_row: np.ndarray, lo: int, hi: int, up: bool, dtype: str, mode: int):
+    """The oracle's quantisation of one group of the oracle's rounded row
+    with its largest-magnitude elements moved one dtype value up (or down):
+    returns (codes of the group, scale)."""
+    import oracle as orc
+    g = np.array(u_row[lo:hi], dtype=np.uint16)
+    mag = g & 0x7FFF
+    a = int(mag.max())
+    top = 0x7F7F if dtype == "bf16" else 0x7BFF
+    b = a + 1 if up else a - 1
+    if b < 0 or b > top:
+        return None, None
+    sel = mag == a
+    g[sel] = (g[sel] & 0x8000) | np.uint16(b)
+    q, sc = orc.quant(g[None, :], orc.BF16 if dtype == "bf16" else orc.FP16, mode)
+    return q[0], sc[0]
+
+
+def check_quant(gpu_values, gpu_scales, ref_values, ref_scales, mode, name, *, u=None, dtype=None,
+                allowed_scales=None, allowed_codes=None):
+    """Codes and scales of one quantised tensor [M, cols] against the
+    oracle's.  Scales as check_scales.  Where a group's scale is inexact
+    because the GPU rounded the group's largest activation to the
+    neighbouring dtype value (reading R14; an E8M0 step when that crosses a
+    power of two), the group's codes are compared with the oracle's codes of
+    its rounded row with that element moved one dtype value the same way
+    (they change with the scale); every other code with the oracle's.  Then
+    the code rule (equal, or one apart in at most floor(n / 1000)).
+    Returns (codes one apart, inexact scales, list of inexact groups)."""
+    nbad, listed = check_scales(gpu_scales, ref_scales, mode, name + ".scales", u=u, dtype=dtype,
+                                allowed=allowed_scales)
+    ref_codes = np.array(ref_values, dtype=np.uint8, copy=True)
+    listed = list(listed)
+    if listed and u is not None:
+        gs = np.asarray(gpu_scales)
+        rs = np.asarray(ref_scales)
+        M, cols = ref_codes.shape
+        groups = rs.reshape(M, -1).shape[1]
+        width = cols // groups
+        for n_, (i, why) in enumerate(listed):
+            r, j = divmod(i, groups)
+            g_val, r_val = gs.reshape(M, -1)[r, j], rs.reshape(M, -1)[r, j]
+            up = bool(g_val > r_val)
+            q, sc = _moved_group_quant(np.asarray(u)[r], j * width, (j + 1) * width, up, dtype, mode)
+            if q is None:
+                continue
+            s0 = np.asarray(sc).ravel()[0]
+            same = (int(s0) == int(g_val)) if mode == 0 else \
+                (np.float32(s0).view(np.uint32) == np.float32(g_val).view(np.uint32))
+            if same:
+                ref_codes[r, j * width:(j + 1) * width] = q
+                if mode == 0:
+                    listed[n_] = (i, "R14: E8M0 step, amax one dtype value away")
+            elif mode == 0:
+                raise AssertionError(f"{name}: E8M0 step at group {i} not explained by a one-value "
+                                     f"move of the group's largest activation")
+    n1 = check_codes(gpu_values, ref_codes, name + ".codes", allowed=allowed_codes)
+    return n1, nbad, listed
 
 
 def scales_u8_or_f32(t):

@@ -10,7 +10,7 @@ import torch
 
 import activation_fp8_quant_amd as afq
 import oracle as orc
-from tests._compare import check_codes, check_dtype16, check_scales, scales_u8_or_f32
+from tests._compare import check_dtype16, check_quant, scales_u8_or_f32
 
 TORCH16 = {"bf16": torch.bfloat16, "fp16": torch.float16}
 ORC_DT = {"bf16": orc.BF16, "fp16": orc.FP16}
@@ -55,9 +55,9 @@ def check_norm(gpu: dict, ref: dict, mode: str, dtype: str, name: str, requant=T
         assert bad.size == 0, f"{name}: {bad.size} scales differ (fp32-direct is exact), first at {bad[:5]}"
         stats["exact"] = True
         return stats
-    stats["codes_1"] = check_codes(gpu["values"], ref["values"], name + ".codes")
-    stats["scales_bad"], listed = check_scales(gpu["scales"], ref["scales"], MODE[mode], name + ".scales",
-                                               u=ref.get("normed"), dtype=dtype)
+    stats["codes_1"], stats["scales_bad"], listed = check_quant(
+        gpu["values"], gpu["scales"], ref["values"], ref["scales"], MODE[mode], name,
+        u=ref.get("normed"), dtype=dtype)
     if listed:
         stats["inexact_scales"] = listed
     if requant and gpu.get("normed") is not None:

@@ -162,7 +162,7 @@ def quant_fp32scale(u):
     amax = max(abs(x) for x in u)
     A = np.float32(float(amax))
     s = np.float32(A / np.float32(448.0))
-    if amax == 0:
+    if s == 0:          # all zero, or amax / 448 below half the least subnormal
         return [0] * len(u), s
     codes = []
     for x in u:

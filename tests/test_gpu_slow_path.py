@@ -1,15 +1,16 @@
 """The fp32-scale quantiser's slow path on the GPU (1x128 and per-token).
 
-Group maxima below 2^-116 leave the fast scale (a corrected product and a
-corrected hardware reciprocal): between 448 * 2^-126 and 2^-116 the scale
-and its reciprocal are IEEE divisions and the quotient is still the
-corrected product; below 448 * 2^-126 the scale is an fp32 subnormal and
-every code is an IEEE division followed by the clamp.  These tests put
-group maxima on both sides of both boundaries and deep in the subnormal
-range, through the standalone quantiser (bf16 and fp32 rows) and through the
-norm (standard RMSNorm whose weights are tiny, so that the normed rows are),
-and compare with the oracle.  Tiny-amax groups are the "tiny" blocks of
-[P1] "Test Plan / Correctness"."""
+Group maxima below 2^-83 leave the fast path (a corrected product for the
+scale, a corrected hardware reciprocal and a corrected quotient): the scale
+and every quotient are IEEE divisions followed by the clamp.  Below
+448 * 2^-126 the scale is an fp32 subnormal, and at or below 224 * 2^-149
+it underflows to 0, which gives all-zero codes (reading R25).  These tests
+put group maxima on both sides of each boundary (and of 2^-116, where the
+scale alone would still be exact) and deep in the subnormal range, through
+the standalone quantiser (bf16 and fp32 rows) and through the norm
+(standard RMSNorm whose weights are tiny, so that the normed rows are), and
+compare with the oracle.  Tiny-amax groups are the "tiny" blocks of [P1]
+"Test Plan / Correctness"."""
 import numpy as np
 import pytest
 import torch
@@ -21,8 +22,10 @@ from tests._gpu import HOST_THREADS, MODE, check_norm, dev16, host8, ref_norm, r
 
 pytestmark = pytest.mark.gpu
 
-BOUND_FAST = 2.0 ** -116          # fast scale from here up
+BOUND_FAST = 2.0 ** -83           # fast path from here up
+BOUND_SCALE = 2.0 ** -116         # the fast scale alone would be exact from here up
 BOUND_NORMAL = 448.0 * 2.0 ** -126  # the scale is an fp32 normal from here up
+BOUND_ZERO = 224.0 * 2.0 ** -149  # the scale underflows to 0 at and below this
 
 
 def _f32_neighbours(x: float, k: int = 3) -> np.ndarray:
@@ -39,10 +42,11 @@ def _bf16_neighbours(x: float, k: int = 2) -> np.ndarray:
 
 def _amax_list(dtype: str) -> np.ndarray:
     if dtype == "fp32":
-        vals = [_f32_neighbours(BOUND_FAST), _f32_neighbours(BOUND_NORMAL),
+        vals = [_f32_neighbours(BOUND_FAST), _f32_neighbours(BOUND_SCALE), _f32_neighbours(BOUND_NORMAL),
+                _f32_neighbours(BOUND_ZERO),
                 np.array([2.0 ** -126, 1e-39, 3e-42, 2.0 ** -149, 2.0 ** -110, 1.0], np.float32)]
     else:
-        vals = [_bf16_neighbours(BOUND_FAST), _bf16_neighbours(BOUND_NORMAL),
+        vals = [_bf16_neighbours(BOUND_FAST), _bf16_neighbours(BOUND_SCALE), _bf16_neighbours(BOUND_NORMAL),
                 np.array([2.0 ** -126, 2.0 ** -130, 2.0 ** -133, 2.0 ** -110, 1.0], np.float32)]
     return np.concatenate(vals).astype(np.float32)
 
@@ -65,8 +69,9 @@ def _rows(amaxes: np.ndarray, width: int, group: int, rng) -> np.ndarray:
 @pytest.mark.parametrize("mode,width", [("b128", 256), ("pt", 256), ("pt", 6144), ("b128", 6144)])
 def test_quant_tiny_amax_around_both_boundaries(dtype, mode, width):
     """fp8_quant (1x128, per-token) on rows whose group maxima straddle
-    2^-116 and 448 * 2^-126 (a few values either side) and lie deep in the
-    subnormals: codes and scales bit-exact against the oracle."""
+    2^-83, 2^-116, 448 * 2^-126 and (fp32) 224 * 2^-149 (a few values either
+    side) and lie deep in the subnormals: codes and scales bit-exact against
+    the oracle."""
     rng = np.random.default_rng(61)
     am = _amax_list(dtype)
     group = 128 if mode == "b128" else width
@@ -89,26 +94,29 @@ def test_quant_tiny_amax_around_both_boundaries(dtype, mode, width):
     bad = np.argwhere(host8(qa.values) != q)
     assert bad.size == 0, [(float(x[tuple(b)]), int(host8(qa.values)[tuple(b)]), int(q[tuple(b)]))
                            for b in bad[:5]]
-    # both sides of both boundaries are present among the group maxima
+    # both sides of the boundaries are present among the group maxima
     s32 = s.ravel()
-    assert (s32 > 0).any() and (s32 < np.float32(2.0 ** -126)).any() and \
-        ((s32 >= np.float32(2.0 ** -126)) & (s32 < np.float32(BOUND_FAST / 448))).any()
+    slow = s32 < np.float32(BOUND_FAST / 448)
+    assert slow.any() and (~slow).any() and (s32 < np.float32(2.0 ** -126)).any() and \
+        ((s32 >= np.float32(2.0 ** -126)) & slow).any()
+    if dtype == "fp32":
+        assert (s32 == 0).any() and (s32 > 0).any()
 
 
 @pytest.mark.parametrize("qin", [0, 1])
 @pytest.mark.parametrize("mode", ["b128", "pt"])
 @pytest.mark.parametrize("M,H", [(64, 4096), (300, 4096), (9, 2048)])
 def test_norm_tiny_weights_slow_path(qin, mode, M, H):
-    """Standard RMSNorm whose weights are U(0.5, 1.5) * 2^k (k = -118,
-    -119, -120, -124): the normed rows are tiny, so group maxima fall on
-    both sides of 2^-116 and of 448 * 2^-126 and below; 1x128 and per-token,
-    at decode and bandwidth row shapes, the default and the fp32-direct
-    quantiser input.  Against the oracle within the contract (fp32-direct:
-    bit-exact)."""
+    """Standard RMSNorm whose weights are U(0.5, 1.5) * 2^k (k = -85,
+    -118, -119, -120, -124): the normed rows are tiny, so group maxima fall
+    on both sides of 2^-83, of 2^-116 and of 448 * 2^-126 and below; 1x128
+    and per-token, at decode and bandwidth row shapes, the default and the
+    fp32-direct quantiser input.  Against the oracle within the contract
+    (fp32-direct: bit-exact)."""
     d = inputs.norm_inputs(M, H, seed=62, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
     w = inputs.bits_to_float(d["w"], "bf16").astype(np.float64)
     seen_slow = seen_sub = 0
-    for k in (-118, -119, -120, -124):
+    for k in (-85, -118, -119, -120, -124):
         wk = inputs.to_bits(w * 2.0 ** k)
         print(f"case tiny-weight norm {mode} qin={qin} M={M} H={H} k={k}", flush=True)
         gpu = run_norm(d["x"], wk, r=d["r"], kind="standard", mode=mode, qin=qin)

@@ -271,3 +271,27 @@ def test_quant_rows_brute_force_fp32_input():
                     codes, sc = brute.quant_fp32scale(u)
                     assert np.float32(s[i, k // G]) == sc
                 assert np.array_equal(ord8(q[i, k:k + G]), ord8(np.array(codes, np.uint8)))
+
+
+def test_fp32_scale_underflow_gives_zero_codes():
+    """Reading R25: a 1x128 / per-token group whose amax / 448 underflows
+    fp32 (amax at most 224 * 2^-149: the quotient is at most half the least
+    subnormal, and the tie goes to the even zero) stores s = 0, and every
+    code is 0x00 as for the all-zero group.  The next amax up stores the
+    least subnormal, and its codes follow the quotient as usual."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.zeros((2, 128), np.float32)
+    x[0, :] = -tiny
+    x[0, 5] = np.float32(224) * tiny
+    x[1, :] = tiny
+    x[1, 9] = np.float32(225) * tiny
+    for mode in (orc.BLOCK128, orc.PER_TOKEN):
+        q, s = orc.quant(x, orc.FP32, mode)
+        assert s[0, 0] == 0 and not np.any(q[0])
+        assert s[1, 0] == tiny
+        assert q[1, 9] == 0x76                              # 225 -> 224 = 1.75 * 2^7
+        assert np.all(q[1, np.arange(128) != 9] == 0x38)    # quotient 1.0
+        # the same through the exact brute force
+        for i in range(2):
+            codes, sc = brute.quant_fp32scale([Fraction(float(t)) for t in x[i]])
+            assert np.float32(s[i, 0]) == sc and list(q[i]) == codes
