@@ -287,12 +287,12 @@ norm_quant_kernel(const NormArgs a)
                 if constexpr (MODE == kMX) {
                     const uint32_t b = e8m0_of(max_quad(amax8(h[k])));
                     q = mx_codes8(h[k], mx_inv_scale(b));
-                    if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b;
+                    if ((lc[k] & 3) == 0) stg_scale(s.scales + row * (s.cols / 32) + lc[k] / 4, b);
                 } else {
                     const Fp32Scale sc = fp32_scale(max_row16(amax8(h[k])));
                     q = fp32scale_codes8(h[k], sc);
                     if ((lc[k] & 15) == 0)
-                        reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc.s;
+                        stg_scale(reinterpret_cast<float *>(s.scales) + row * (s.cols / 128) + lc[k] / 16, sc.s);
                 }
                 stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
             }
@@ -535,14 +535,196 @@ norm_quant_kernel(const NormArgs a)
                 if (!ok[k]) continue;
                 const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
                 if constexpr (MODE == kMX) {
-                    if ((lc[k] & 3) == 0) s.scales[row * (s.cols / 32) + lc[k] / 4] = (uint8_t)b[k];
+                    if ((lc[k] & 3) == 0) stg_scale(s.scales + row * (s.cols / 32) + lc[k] / 4, b[k]);
                 } else {
                     if ((lc[k] & 15) == 0)
-                        reinterpret_cast<float *>(s.scales)[row * (s.cols / 128) + lc[k] / 16] = sc[k].s;
+                        stg_scale(reinterpret_cast<float *>(s.scales) + row * (s.cols / 128) + lc[k] / 16, sc[k].s);
                 }
                 stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q[k]);
             }
         }
+    }
+}
+
+// ============================================ per-token, one wavefront a row
+// Two per-wavefront reductions at once.  v_permlane16_swap(a, b) trades the
+// odd 16-lane rows of a with the even rows of b, so after it a holds rows
+// (a0, b0, a2, b2) and b rows (a1, b1, a3, b3), and their sum is
+// (a0+a1, b0+b1, a2+a3, b2+b3); v_permlane32_swap(x, y) then pairs the lower
+// halves with the upper ones.  With every 16-lane row of the inputs uniform
+// (after sum_row16 / max_row16) this forms the wavefront tree of sum_wave /
+// max_wave -- (r0 + r1) + (r2 + r3) over the row values r -- for two (or
+// four) values at once, operand for operand.
+__device__ __forceinline__ float sum_pair16(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_pair32(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_pair16(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(max((uint32_t)p[0], (uint32_t)p[1]));
+}
+__device__ __forceinline__ float max_pair32(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(max((uint32_t)p[0], (uint32_t)p[1]));
+}
+
+// Per-token rows of 65..256 chunks (widths 520..2048, one or two segments)
+// on one wavefront each, CPL = 2..4 chunks per lane, R = 256 / 64 rows per
+// block.  Everything a row needs stays inside its wavefront: no LDS and no
+// barrier, and the per-row work (two sums of squares, two maxima, the
+// reciprocal square roots and the scales) is done once per row instead of
+// once per wavefront of it.  The numerics are those of norm_quant_kernel at
+// every shape: slot k of the lane is the aligned 64-chunk block k, each
+// block is summed by the wavefront tree and the blocks by the tree of
+// lds_blocks_sum, which for at most four blocks is (b0 + b1) + (b2 + b3)
+// (a missing block adds an exact zero); the block trees of slots 0-1 and
+// 2-3 are formed pairwise (sum_pair16 / sum_pair32), which leaves block k's
+// total in 16-lane row k, and the segment totals come from the same pairing
+// applied to the rows of each segment.  Lanes off the row load chunk 0 of
+// the row's segment and compute on it; only their stores are skipped.
+template <int DT, bool GEMMA, int CPL, int NSEG, bool SEGU>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+norm_pt_wave_kernel(const NormArgs a)
+{
+    static_assert(CPL >= 2 && CPL <= 4, "one wavefront holds at most 4 blocks of 64 chunks");
+    const int t = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * a.R + wave;
+    if (row >= a.M) return; // the whole wavefront: nothing waits for it
+    const bool has_res = NSEG == 1 && a.res_in != nullptr; // two segments take no residual
+    const uint8_t *xrow0 = a.seg[0].x + row * a.seg[0].x_pitch;
+    const uint8_t *xrow1 = NSEG > 1 ? a.seg[1].x + row * a.seg[1].x_pitch : xrow0;
+    const int64_t rrow = row * a.C0 * 16;
+
+    // ---- issue every load of the row
+    uint4 xv[CPL], rv[CPL], wv[CPL];
+    bool ok[CPL];
+    int sg[CPL], lc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = t + 64 * k;
+        ok[k] = c < a.C;
+        if constexpr (NSEG == 1) {
+            sg[k] = 0;
+            lc[k] = c;
+        } else {
+            sg[k] = (SEGU ? 64 * k : c) >= a.C0 ? 1 : 0;
+            lc[k] = c - (sg[k] ? a.C0 : 0);
+        }
+        const int ls = ok[k] ? lc[k] : 0;
+        const bool s1 = NSEG > 1 && (SEGU ? sg[k] != 0 : (ok[k] && sg[k] != 0));
+        xv[k] = ldg_stream((s1 ? xrow1 : xrow0) + ls * 16);
+        wv[k] = ldg<uint4>((s1 ? a.seg[1].w : a.seg[0].w) + ls * 16);
+        if (has_res) rv[k] = ldg_stream(a.res_in + rrow + ls * 16);
+    }
+
+    // ---- residual add (h = round_dt(x + r), stored), squares per chunk.
+    //      Rows stay packed in the dtype (hp) between the steps, which keeps
+    //      the kernel within 64 VGPRs: eight wavefronts per SIMD, so that a
+    //      round of the GPU holds 32 rows per compute unit.
+    uint4 hp[CPL];
+    float sq[CPL];            // this lane's chunk of slot k: its sum of squares
+    float sq0[CPL], sq1[CPL]; // the same split by segment (two segments, unaligned)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        hp[k] = xv[k];
+        if (has_res) {
+            float hf[8], rf[8];
+            unpack8<DT>(xv[k], hf);
+            unpack8<DT>(rv[k], rf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hf[i] += rf[i];
+            hp[k] = pack8<DT>(hf);
+            if (ok[k]) stg_stream(a.res_out + rrow + lc[k] * 16, hp[k]);
+        }
+        sq[k] = ok[k] ? sumsq8<DT>(hp[k], 0.f) : 0.f;
+        sq0[k] = sg[k] ? 0.f : sq[k];
+        sq1[k] = sg[k] ? sq[k] : 0.f;
+    }
+
+    // ---- block totals: block k's in 16-lane row k (blocks past the row are 0)
+    auto block_rows = [](const float (&v)[CPL]) -> float {
+        float r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = k < CPL ? sum_row16(v[k]) : 0.f;
+        return sum_pair32(sum_pair16(r[0], r[1]), sum_pair16(r[2], r[3]));
+    };
+    // ---- segment totals: (b0 + b1) + (b2 + b3) over the blocks of a segment
+    const int blk = t >> 4; // the block whose total this lane's 16-lane row holds
+    float t0, t1 = 0.f;
+    if constexpr (NSEG == 1) {
+        const float b = block_rows(sq);
+        const float p = sum_pair16(b, b); // rows: b0+b1, b0+b1, b2+b3, b2+b3
+        t0 = lane_pick(sum_pair32(p, p), 0);
+    } else if constexpr (SEGU) {
+        // a block lies in one segment: split the block totals by rows
+        const float b = block_rows(sq);
+        const bool in1 = 64 * blk >= a.C0;
+        const float p = sum_pair16(in1 ? 0.f : b, in1 ? b : 0.f); // rows: s0(01), s1(01), s0(23), s1(23)
+        const float q = sum_pair32(p, p);                         // rows: s0, s1, s0, s1
+        t0 = lane_pick(q, 0);
+        t1 = lane_pick(q, 16);
+    } else {
+        const float b0 = block_rows(sq0), b1 = block_rows(sq1);
+        const float p = sum_pair16(b0, b1);
+        const float q = sum_pair32(p, p);
+        t0 = lane_pick(q, 0);
+        t1 = lane_pick(q, 16);
+    }
+    const float inv0 = rsqrt_nr(__builtin_fmaf(t0, a.inv_cols0, a.eps));
+    const float inv1 = NSEG > 1 ? rsqrt_nr(__builtin_fmaf(t1, a.inv_cols1, a.eps)) : inv0;
+
+    // ---- u = round_dt(h * inv * g), kept packed; optional copy.  The row
+    //      maximum is taken of |h * inv * g| before the rounding and rounded
+    //      once: rounding to nearest is monotone and symmetric, so that is
+    //      the largest |u|.
+    uint4 up[CPL];
+    float am0 = 0.f, am1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const float inv = sg[k] ? inv1 : inv0;
+        float hf[8], wf[8];
+        unpack8<DT>(hp[k], hf);
+        unpack8<DT>(wv[k], wf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            hf[i] *= GEMMA ? __builtin_fmaf(wf[i], inv, inv) : wf[i] * inv;
+        up[k] = pack8<DT>(hf);
+        uint8_t *normed = sg[k] ? a.seg[1].normed : a.seg[0].normed;
+        const int32_t cols = sg[k] ? a.seg[1].cols : a.seg[0].cols;
+        if (normed && ok[k]) stg_stream(normed + (row * cols + (int64_t)lc[k] * 8) * 2, up[k]);
+        const float m = ok[k] ? amax8(hf) : 0.f;
+        if (NSEG > 1 && sg[k]) am1 = __builtin_fmaxf(am1, m); else am0 = __builtin_fmaxf(am0, m);
+    }
+    if constexpr (NSEG == 1) {
+        am0 = lane_pick(max_wave(am0), 0);
+    } else {
+        const float p = max_pair16(max_row16(am0), max_row16(am1)); // rows: m0(01), m1(01), m0(23), m1(23)
+        const float q = max_pair32(p, p);                           // rows: m0, m1, m0, m1
+        am0 = lane_pick(q, 0);
+        am1 = lane_pick(q, 16);
+    }
+    const Fp32Scale sc0 = fp32_scale(round_dt<DT>(am0));
+    const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(round_dt<DT>(am1)) : sc0;
+
+    // ---- quantise, store
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
+        float u[8];
+        unpack8<DT>(up[k], u);
+        const uint2 q = fp32scale_codes8(u, sg[k] ? sc1 : sc0);
+        if (!ok[k]) continue;
+        stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+        if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
     }
 }
 
@@ -577,6 +759,30 @@ static hipError_t go_norm_kind(const NormArgs &a, bool gemma, int nseg, int CPL,
 {
     return gemma ? go_norm_cpl<DT, MODE, true, F32Q>(a, nseg, CPL, st)
                  : go_norm_cpl<DT, MODE, false, F32Q>(a, nseg, CPL, st);
+}
+
+template <int DT, bool GEMMA, int CPL>
+static hipError_t go_norm_pt_wave(const NormArgs &a, int nseg, hipStream_t st)
+{
+    const int64_t blocks = (a.M + a.R - 1) / a.R;
+    const dim3 grid((unsigned)blocks), block(64 * a.R);
+    if (nseg == 1)
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 1, false>), grid, block, 0, st, a);
+    else if (a.C0 % 64 == 0)
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, false>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t go_norm_pt_wave_cpl(const NormArgs &a, bool gemma, int nseg, int CPL, hipStream_t st)
+{
+    switch (CPL) {
+    case 2: return gemma ? go_norm_pt_wave<DT, true, 2>(a, nseg, st) : go_norm_pt_wave<DT, false, 2>(a, nseg, st);
+    case 3: return gemma ? go_norm_pt_wave<DT, true, 3>(a, nseg, st) : go_norm_pt_wave<DT, false, 3>(a, nseg, st);
+    default: return gemma ? go_norm_pt_wave<DT, true, 4>(a, nseg, st) : go_norm_pt_wave<DT, false, 4>(a, nseg, st);
+    }
 }
 
 // The fp32-direct variant exists for the 1x128 and per-token modes only
@@ -638,6 +844,10 @@ int launch_norm(const NormPlan &p, void *stream)
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
     const bool f32q = p.qin == 1;
+    // per-token rows on one wavefront at two to four chunks per lane: the
+    // kernel without LDS or barrier (the fp32-direct form keeps the general
+    // kernel, whose fp64 reduction it has)
+    const bool pt_wave = mode == kPT && !f32q && sh.WPR == 1 && sh.CPL >= 2;
     // one launch per row slice (a single one below ~2^31 / NT rows)
     const int64_t step = row_rows_per_launch(a.NT, a.R);
     NormArgs b = a;
@@ -652,8 +862,13 @@ int launch_norm(const NormPlan &p, void *stream)
         }
         b.res_in = a.res_in ? a.res_in + r0 * a.C0 * 16 : nullptr;
         b.res_out = a.res_out ? a.res_out + r0 * a.C0 * 16 : nullptr;
-        const hipError_t e = p.dtype == kFP16 ? go_norm_mode<kFP16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st)
-                                              : go_norm_mode<kBF16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st);
+        hipError_t e;
+        if (pt_wave)
+            e = p.dtype == kFP16 ? go_norm_pt_wave_cpl<kFP16>(b, gemma, p.nseg, sh.CPL, st)
+                                 : go_norm_pt_wave_cpl<kBF16>(b, gemma, p.nseg, sh.CPL, st);
+        else
+            e = p.dtype == kFP16 ? go_norm_mode<kFP16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st)
+                                 : go_norm_mode<kBF16>(b, mode, f32q, gemma, p.nseg, sh.CPL, st);
         if (e != hipSuccess) return (int)e;
     }
     return 0;

@@ -107,6 +107,8 @@ static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool m
     if (per_token) {
         if (M <= 256) {
             cpl = C > 256 ? 2 : 1;
+        } else if (C > 64 && C <= 256) {
+            cpl = (C + 63) / 64; // one wavefront a row
         } else {
             cpl = 2;
             for (int c = 2; c <= 4; ++c)

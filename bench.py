@@ -203,6 +203,13 @@ class NormCase:
                                          residual=s["r"], residual_out=s["rout"], out=s["out"],
                                          quant_input=self.qin, quantize=self.quantize)
 
+    def prepared(self):
+        """The same launch on buffer set 0, marshalled once (afq.prepare)."""
+        s = self.sets[0]
+        return self.afq.prepare(self.afq.fused_add_rmsnorm_quant, s["x"], self.w, 1e-6, mode=self.mode,
+                                kind=self.kind, residual=s["r"], residual_out=s["rout"], out=s["out"],
+                                quant_input=self.qin, quantize=self.quantize)
+
 
 class SiluCase:
     """SiLU-and-mul + quant, or with swiglu = (alpha, beta, limit) the
@@ -238,6 +245,15 @@ class SiluCase:
         g, out = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
         self._launch(g, out)
+
+    def prepared(self):
+        """The same launch on buffer set 0, marshalled once (afq.prepare)."""
+        g, out = self.sets[0]
+        if self.swiglu:
+            return self.afq.prepare(self.afq.swiglu_oai_quant, g, *self.swiglu, out=out,
+                                    quant_input=self.qin, quantize=self.quantize)
+        return self.afq.prepare(self.afq.silu_mul_quant, g, self.mode, out=out, quant_input=self.qin,
+                                quantize=self.quantize)
 
 
 class TwoSegCase:
@@ -375,7 +391,9 @@ def rotation_sets(ws_bytes, target=1 << 30):
 
 def eager_single_us(fn, reps=50):
     """us of one launch timed alone: events around it on an idle GPU,
-    median over `reps` (includes the launch latency)."""
+    median over `reps` (includes the launch latency and the host's time to
+    issue it: the binding's checks and marshalling, or for a prepared launch
+    only the C call)."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -420,6 +438,7 @@ def run_sweep():
             r["pct_hbm_peak"] = round(100 * case.bytes / us / 1e3 / HBM_PEAK_GBS, 1)
         if "eager" in extra:
             extra["eager_single_us"] = round(eager_single_us(case), 2)
+            extra["eager_single_prepared_us"] = round(eager_single_us(case.prepared()), 2)
             del extra["eager"]
         r.update(extra)
         out.append(r)
