@@ -590,11 +590,18 @@ __device__ __forceinline__ float max_pair32(float a, float b)
 // total in 16-lane row k, and the segment totals come from the same pairing
 // applied to the rows of each segment.  Lanes off the row load chunk 0 of
 // the row's segment and compute on it; only their stores are skipped.
-template <int DT, bool GEMMA, int CPL, int NSEG, bool SEGU>
+//
+// KB: 0 for one segment; for two segments whose boundary lies on a 64-chunk
+// line, the first slot of the second segment (1..3), so that every slot's
+// segment, scale and pointers are known at compile time; -1 for two
+// segments with the boundary inside a slot (segment chosen per lane).
+template <int DT, bool GEMMA, int CPL, int NSEG, int KB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 norm_pt_wave_kernel(const NormArgs a)
 {
     static_assert(CPL >= 2 && CPL <= 4, "one wavefront holds at most 4 blocks of 64 chunks");
+    static_assert((NSEG == 1) == (KB == 0) && KB >= -1 && KB < CPL, "segment boundary slot");
+    constexpr bool SEGU = KB > 0;
     const int t = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = (int64_t)blockIdx.x * a.R + wave;
@@ -615,8 +622,11 @@ norm_pt_wave_kernel(const NormArgs a)
         if constexpr (NSEG == 1) {
             sg[k] = 0;
             lc[k] = c;
+        } else if constexpr (SEGU) {
+            sg[k] = k >= KB ? 1 : 0;
+            lc[k] = k >= KB ? t + 64 * (k - KB) : c;
         } else {
-            sg[k] = (SEGU ? 64 * k : c) >= a.C0 ? 1 : 0;
+            sg[k] = c >= a.C0 ? 1 : 0;
             lc[k] = c - (sg[k] ? a.C0 : 0);
         }
         const int ls = ok[k] ? lc[k] : 0;
@@ -658,7 +668,6 @@ norm_pt_wave_kernel(const NormArgs a)
         return sum_pair32(sum_pair16(r[0], r[1]), sum_pair16(r[2], r[3]));
     };
     // ---- segment totals: (b0 + b1) + (b2 + b3) over the blocks of a segment
-    const int blk = t >> 4; // the block whose total this lane's 16-lane row holds
     float t0, t1 = 0.f;
     if constexpr (NSEG == 1) {
         const float b = block_rows(sq);
@@ -667,7 +676,7 @@ norm_pt_wave_kernel(const NormArgs a)
     } else if constexpr (SEGU) {
         // a block lies in one segment: split the block totals by rows
         const float b = block_rows(sq);
-        const bool in1 = 64 * blk >= a.C0;
+        const bool in1 = (t >> 4) >= KB; // this lane's 16-lane row holds block t >> 4
         const float p = sum_pair16(in1 ? 0.f : b, in1 ? b : 0.f); // rows: s0(01), s1(01), s0(23), s1(23)
         const float q = sum_pair32(p, p);                         // rows: s0, s1, s0, s1
         t0 = lane_pick(q, 0);
@@ -766,12 +775,20 @@ static hipError_t go_norm_pt_wave(const NormArgs &a, int nseg, hipStream_t st)
 {
     const int64_t blocks = (a.M + a.R - 1) / a.R;
     const dim3 grid((unsigned)blocks), block(64 * a.R);
+    // two segments with the boundary on a 64-chunk line: its slot, 1..CPL-1
+    // (the first segment holds at least one block, the second at least one
+    // chunk of the last slot)
+    const int kb = (nseg == 2 && a.C0 % 64 == 0) ? a.C0 / 64 : 0;
     if (nseg == 1)
-        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 1, false>), grid, block, 0, st, a);
-    else if (a.C0 % 64 == 0)
-        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 1, 0>), grid, block, 0, st, a);
+    else if (kb == 1)
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, 1>), grid, block, 0, st, a);
+    else if (kb == 2 && CPL > 2)
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, (CPL > 2 ? 2 : 1)>), grid, block, 0, st, a);
+    else if (kb == 3 && CPL > 3)
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, (CPL > 3 ? 3 : 1)>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((norm_pt_wave_kernel<DT, GEMMA, CPL, 2, -1>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

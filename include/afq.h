@@ -190,6 +190,13 @@ enum { AFQ_QIN_DEFAULT = 0, AFQ_QIN_FP32 = 1, AFQ_QIN_BF16 = 2 };
  *           activation dtype (the norm output u, or for SiLU-and-mul the
  *           bf16 activation); NULL = not written.  Required by a copy-only
  *           launch.
+ * The tags that the pages' quantised-activation tuples carry beside codes
+ * and scales -- the mode, the original dtype and shape (vLLM pull request
+ * 65479, QuantizedActivation; SGLang pull request 34502, "Change") -- are
+ * not repeated here: the caller owns this struct and has just passed each
+ * of them in the descriptor (mode, dtype, M and cols), and the library
+ * writes nothing but device buffers.  The Python binding's result object
+ * carries them.
  */
 typedef struct afq_qact {
     void *values;

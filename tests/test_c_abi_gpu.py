@@ -1,5 +1,5 @@
 """The C ABI used from plain C (tests/c_abi/afq_c_example.c): a C program
-with no Python or torch allocates with hipMalloc, calls the three entry
+with no Python or torch allocates with hipMalloc, calls the four entry
 points and checks the outputs against the C oracle linked into it.  It is
 built by __graft_entry__.build() and run here as a child process."""
 import os
