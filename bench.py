@@ -701,8 +701,10 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-# The GPU hosts give each GPU's jobs a share of 16 cores, whatever the
-# machine's core count: the oracle's row threads are capped there.
+# The oracle's row threads are capped at 16: a process that drives one GPU
+# is commonly given a share of a larger machine's cores, and the cap keeps
+# the baseline comparable between machines.  The record states the cap,
+# the machine's CPU count and the CPUs this process may use.
 CPU_THREAD_CAP = 16
 
 

@@ -16,7 +16,8 @@ TORCH16 = {"bf16": torch.bfloat16, "fp16": torch.float16}
 ORC_DT = {"bf16": orc.BF16, "fp16": orc.FP16}
 MODE = {"mx": afq.MXFP8, "b128": afq.BLOCK128, "pt": afq.PER_TOKEN}
 KIND = {"gemma": afq.GEMMA, "standard": afq.STANDARD}
-# host threads for the oracle (the GPU hosts give a process 16 cores)
+# host threads for the oracle (at most 16: a process driving one GPU is
+# commonly given a share of the machine's cores)
 HOST_THREADS = max(1, min(os.cpu_count() or 1, 16))
 
 

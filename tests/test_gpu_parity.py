@@ -155,7 +155,7 @@ def test_norm_row_shapes_by_size(mode, H, M, dtype):
 
 @pytest.mark.parametrize("mode,H,Ms,qin", [
     ("pt", 6144, (8, 300, 1100), 0),     # 2, 3, 3 chunks per lane
-    ("pt", 2048, (8, 300, 1100), 0),     # 1 chunk per lane, then 2 with two rows per block
+    ("pt", 2048, (8, 300, 1100), 0),     # 1 chunk per lane, then one wavefront a row (4 per lane)
     ("pt", 8192, (8, 300), 1),           # fp32-direct: 2 chunks per lane, 512 then 512 lanes
     ("mx", 6144, (8, 1024, 1536), 0),    # 1, 2, 3 chunks per lane
     ("mx", 4096, (8, 1536, 3072), 0),    # 1, 2, 4 chunks per lane (two rows per block)
@@ -260,6 +260,36 @@ def test_two_segment_unaligned_boundary(mode, widths, qin, M):
         ref = ref_norm(sg["x"], sg["w"], kind="standard", mode=mode, qin=qin)
         name = f"two-seg {widths} {mode} qin={qin} M={M}"
         _report(name, check_norm(gpu, ref, mode, "bf16", name, requant=(qin == 0), qin=qin))
+
+
+@pytest.mark.parametrize("widths,dtype", [((1536, 512), "bf16"), ((1536, 512), "fp16"), ((512, 1536), "bf16"),
+                                          ((1024, 1024), "bf16"), ((1000, 512), "bf16"), ((8, 2040), "bf16")])
+def test_two_segment_rows_independent_of_launch_shape(widths, dtype):
+    """Two per-token segments: 8 rows run on the multi-wavefront kernel (one
+    chunk per lane), 300 and 1100 rows on one wavefront a row, with the
+    segment boundary in slot 3, 1 or 2 (1536 + 512, 512 + 1536, 1024 + 1024)
+    or inside a slot (1000 + 512, 8 + 2040).  The first 8 rows of every
+    launch are bit-identical (codes, scales, copy), and against the oracle."""
+    print(f"case two-seg shape invariance {widths} {dtype}", flush=True)
+    segs = inputs.two_segment_inputs(1100, widths, seed=43, dtype=dtype)
+    first = None
+    for M in (8, 300, 1100):
+        xs = [dev16(sg["x"][:M], dtype) for sg in segs]
+        ws = [dev16(sg["w"], dtype) for sg in segs]
+        outs = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=afq.PER_TOKEN, kind=afq.STANDARD,
+                                           want_normed=True)
+        torch.cuda.synchronize()
+        rows = [dict(normed=host16(qa.normed)[:8], values=host8(qa.values)[:8],
+                     scales=scales_u8_or_f32(qa.scales)[:8]) for qa in outs]
+        if first is None:
+            first = rows
+            for sg, g in zip(segs, rows):
+                ref = ref_norm(sg["x"][:8], sg["w"], kind="standard", mode="pt", dtype=dtype)
+                check_norm(g, ref, "pt", dtype, f"two-seg-shape {widths}")
+        for i, (a, b) in enumerate(zip(rows, first)):
+            for k in a:
+                assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), \
+                    (widths, M, i, k)
 
 
 # ----------------------------------------------------------- SiLU-and-mul
