@@ -113,9 +113,12 @@ __device__ __forceinline__ float clamp448(float v)
 // two 32-bit words (v_cvt_pk_fp8_f32 writes two codes into one half).
 __device__ __forceinline__ uint2 cvt8_e4m3(const float (&v)[8])
 {
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    // the first conversion of each word keeps the upper half of its `old`
+    // operand, which the second overwrites: any register serves, and v[0] /
+    // v[4] (read by the same instruction) save a move of a zero
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], __float_as_int(v[0]), false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], __float_as_int(v[4]), false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
     return make_uint2((uint32_t)w0, (uint32_t)w1);
 }
@@ -331,6 +334,40 @@ __device__ __forceinline__ float rsqrt_nr(float x)
 {
     const float y = __builtin_amdgcn_rsqf(x);
     return y * __builtin_fmaf(-0.5f * x, y * y, 1.5f);
+}
+
+// The inverse RMS of the fp32-direct norm: fl32(1 / sqrt(ss / cols + eps))
+// with the division, the sum, the square root and the reciprocal each the
+// IEEE fp64 operation (the formula evaluated as written in fp64), given
+// rcols = RN64(1 / cols).  Those IEEE operations cost some thirty fp64
+// instructions on the row's critical path; the fast path below needs about
+// a third of that and gives the same fp32:
+//   x = fl64(ss * rcols + eps) is within 2^-51 (relative) of the formula's
+//   fp64 argument, and the formula's fp64 result within 2^-52 of the exact
+//   1/sqrt of that argument.  z is the hardware estimate of 1/sqrt(x) after
+//   two Newton steps; it is accepted only if the residual 1 - x z^2 (one
+//   FMA, error about 2^-52) is below 2^-46 in magnitude, which bounds z to
+//   within about 2^-47 of 1/sqrt(x) whatever the estimate's accuracy.  The
+//   formula's result then lies in [z (1 - 2^-44), z (1 + 2^-44)], and if
+//   both ends round to the same fp32, so does it (rounding is monotone).
+// Otherwise -- a value within about 2^-44 of an fp32 rounding midpoint, one
+// row in 10^6 or so, or anything non-finite -- the formula itself runs.
+// `fast`, when given, reports which path gave the result.
+__device__ __forceinline__ float inv_rms_f32q(double ss, int32_t cols, double rcols, float eps,
+                                              bool *fast = nullptr)
+{
+    const double x = __builtin_fma(ss, rcols, (double)eps);
+    const double hx = 0.5 * x;
+    double z = __builtin_amdgcn_rsq(x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) z = __builtin_fma(z, __builtin_fma(-(hx * z), z, 0.5), z);
+    const double e = __builtin_fma(-(x * z), z, 1.0);
+    const float lo = (float)(z * (1.0 - 0x1p-44));
+    const float hi = (float)(z * (1.0 + 0x1p-44));
+    const bool ok = __builtin_fabs(e) < 0x1p-46 && lo == hi;
+    if (fast) *fast = ok;
+    if (__builtin_expect(ok, 1)) return lo;
+    return (float)(1.0 / sqrt(ss / (double)cols + (double)eps));
 }
 
 // largest |u| of 8 values (v_max3_f32 with |.| source modifiers)

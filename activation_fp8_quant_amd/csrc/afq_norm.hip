@@ -38,6 +38,8 @@ struct NormArgs {
     int32_t wpr_shift; // log2(WPR) when R > 1
     float inv_cols0;   // 1 / cols of each segment (the mean of the squares)
     float inv_cols1;
+    double rcols0;     // RN64(1 / cols) of each segment (fp32-direct inverse RMS)
+    double rcols1;
 };
 
 // sum of squares of the 8 values of a packed chunk (v_dot2 on pairs)
@@ -77,8 +79,8 @@ __device__ __forceinline__ float sumsq8(const uint4 &c, float acc)
 // dtype rounding, with inv32 = fl32(1 / sqrt(mean(h^2) + eps)).  To make
 // inv32 the correctly rounded value (so that y, and with it every scale and
 // code, is reproducible) the sum of squares is accumulated in fp64 (each
-// h^2 is exact there) and the square root and reciprocal are fp64 IEEE
-// operations rounded once to fp32.
+// h^2 is exact there) and the square root and reciprocal are those of fp64
+// IEEE operations rounded once to fp32 (inv_rms_f32q).
 //
 // SEGU (two segments only): the first segment's chunk count C0 is a
 // multiple of 64, so the chunks of slot k of a wavefront (64 consecutive
@@ -201,8 +203,8 @@ norm_quant_kernel(const NormArgs a)
                 lds_barrier();
                 sd0 = lds_rows_sum_f64<NSEG>(&redd[0][p0], &redd[1][p0], a.WPR, sd1);
             }
-            inv0 = (float)(1.0 / sqrt(sd0 / (double)a.seg[0].cols + (double)a.eps));
-            inv1 = NSEG > 1 ? (float)(1.0 / sqrt(sd1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
+            inv0 = inv_rms_f32q(sd0, a.seg[0].cols, a.rcols0, a.eps);
+            inv1 = NSEG > 1 ? inv_rms_f32q(sd1, a.seg[1].cols, a.rcols1, a.eps) : inv0;
         } else {
             __shared__ float red[2][kMaxBlock / 64];
             if (has0) ss0 = sum_wave(ss0);
@@ -419,8 +421,8 @@ norm_quant_kernel(const NormArgs a)
             }
             lds_barrier();
             t0 = lds_blocks_sum_f64<NSEG>(&redd[0][pb], &redd[1][pb], NB, t1);
-            inv0 = (float)(1.0 / sqrt(t0 / (double)a.seg[0].cols + (double)a.eps));
-            inv1 = NSEG > 1 ? (float)(1.0 / sqrt(t1 / (double)a.seg[1].cols + (double)a.eps)) : inv0;
+            inv0 = inv_rms_f32q(t0, a.seg[0].cols, a.rcols0, a.eps);
+            inv1 = NSEG > 1 ? inv_rms_f32q(t1, a.seg[1].cols, a.rcols1, a.eps) : inv0;
         } else {
             __shared__ float red[2][64];
             float t0, t1;
@@ -724,15 +726,32 @@ norm_pt_wave_kernel(const NormArgs a)
     const Fp32Scale sc0 = fp32_scale(round_dt<DT>(am0));
     const Fp32Scale sc1 = NSEG > 1 ? fp32_scale(round_dt<DT>(am1)) : sc0;
 
-    // ---- quantise, store
+    // ---- quantise, store.  The fast/slow choice is made once for the row
+    //      (both segments fast: the common case) rather than per chunk.
+    uint2 qv[CPL];
+    if (sc0.fast && sc1.fast) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            float u[8];
+            unpack8<DT>(up[k], u);
+            const Fp32Scale &sc = sg[k] ? sc1 : sc0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = quotient_fast(u[i], sc);
+            qv[k] = cvt8_e4m3(u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            float u[8];
+            unpack8<DT>(up[k], u);
+            qv[k] = fp32scale_codes8(u, sg[k] ? sc1 : sc0);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const NormSegPlan &s = sg[k] ? a.seg[1] : a.seg[0];
-        float u[8];
-        unpack8<DT>(up[k], u);
-        const uint2 q = fp32scale_codes8(u, sg[k] ? sc1 : sc0);
         if (!ok[k]) continue;
-        stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, q);
+        stg_stream(s.values + row * s.cols + (int64_t)lc[k] * 8, qv[k]);
         if (lc[k] == 0) reinterpret_cast<float *>(s.scales)[row] = sg[k] ? sc1.s : sc0.s;
     }
 }
@@ -858,6 +877,8 @@ int launch_norm(const NormPlan &p, void *stream)
     a.wpr_shift = sh.WPR == 2 ? 1 : 0; // R > 1 only with one or two wavefronts per row
     a.inv_cols0 = 1.0f / (float)p.seg[0].cols;
     a.inv_cols1 = 1.0f / (float)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
+    a.rcols0 = 1.0 / (double)p.seg[0].cols;
+    a.rcols1 = 1.0 / (double)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
     const bool f32q = p.qin == 1;

@@ -13,6 +13,8 @@
 //   afqp_e4m3_range the same on every fp32 bit pattern base .. base + n - 1,
 //                  generated in the kernel
 //   afqp_pack_bf16 pack8<bf16> on 8 values at a time (v_cvt_pk_bf16_f32)
+//   afqp_inv_rms   inv_rms_f32q(ss, cols, RN64(1/cols), eps): the
+//                  fp32-direct inverse RMS, and which path gave it
 //
 // Every kernel is guarded by its element count; the host wrappers reject
 // counts above 2^31, counts that are not a multiple of 8 where 8 values go
@@ -73,6 +75,16 @@ __global__ void __launch_bounds__(kBlock) k_pack_bf16(const float *v, uint16_t *
     *reinterpret_cast<uint4 *>(out + i * 8) = pack8<kBF16>(x);
 }
 
+__global__ void __launch_bounds__(kBlock) k_inv_rms(const double *ss, int32_t cols, double rcols, float eps,
+                                                    float *inv, uint8_t *fast, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    bool f = false;
+    inv[i] = inv_rms_f32q(ss[i], cols, rcols, eps, &f);
+    fast[i] = f ? 1 : 0;
+}
+
 // threads needed for n work items, or -1 when n is out of range
 int64_t grid_for(int64_t n)
 {
@@ -130,6 +142,18 @@ int afqp_e4m3_range(uint32_t base, uint8_t *codes, int64_t n, void *stream)
 }
 
 // n must be a multiple of 8; out holds n bf16 bit patterns
+// inv[i] = inv_rms_f32q(ss[i], cols, RN64(1/cols), eps); fast[i] = 1 where
+// the fast path gave it.  cols must be positive.
+int afqp_inv_rms(const double *ss, int32_t cols, float eps, float *inv, uint8_t *fast, int64_t n, void *stream)
+{
+    const int64_t g = grid_for(n);
+    if (g < 0 || cols <= 0) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_inv_rms, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, ss, cols,
+                       1.0 / (double)cols, eps, inv, fast, n);
+    return (int)hipGetLastError();
+}
+
 int afqp_pack_bf16(const float *v, uint16_t *out, int64_t n, void *stream)
 {
     if (n % 8 || !aligned16(v) || !aligned16(out)) return -1;

@@ -20,7 +20,11 @@ applies the library's own device primitives element-wise):
   * v_cvt_pk_bf16_f32 on every bf16 neighbourhood of the fp32 line: each of
     the 2^16 upper halves with the lower halves that decide round to nearest
     even (0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF and two random), against the
-    oracle's bf16 rounding.
+    oracle's bf16 rounding;
+  * the fp32-direct norm's inverse RMS fl32(1 / sqrt(ss / cols + eps)) (its
+    fast path and the fallback to the fp64 formula) against the formula in
+    numpy float64, on random sums and on sums whose result sits on an fp32
+    rounding midpoint.
 """
 import concurrent.futures
 import ctypes
@@ -48,7 +52,9 @@ def _probe():
     L.afqp_cvt8_e4m3.argtypes = [P, P, I64, P]
     L.afqp_e4m3_range.argtypes = [ctypes.c_uint32, P, I64, P]
     L.afqp_pack_bf16.argtypes = [P, P, I64, P]
-    for f in (L.afqp_scale, L.afqp_quotient, L.afqp_cvt8_e4m3, L.afqp_e4m3_range, L.afqp_pack_bf16):
+    L.afqp_inv_rms.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, I64, P]
+    for f in (L.afqp_scale, L.afqp_quotient, L.afqp_cvt8_e4m3, L.afqp_e4m3_range, L.afqp_pack_bf16,
+              L.afqp_inv_rms):
         f.restype = ctypes.c_int
     return L
 
@@ -223,3 +229,46 @@ def test_cvt_bf16_round_to_nearest_even_classes():
     want = orc.round_bf16(v[:bits.size].astype(np.float64))
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, [(hex(int(bits[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+@pytest.mark.parametrize("cols,eps", [(4096, 1e-6), (2048, 1e-6), (1536, 1e-6), (512, 1e-6), (6144, 1e-5),
+                                      (2176, 0.0), (7168, 1e-6)])
+def test_fp32_direct_inverse_rms(cols, eps):
+    """The fp32-direct norm's inverse RMS, inv_rms_f32q(ss, cols, eps),
+    against fl32(1 / sqrt(ss / cols + eps)) evaluated in numpy float64
+    (IEEE division, sum, square root and reciprocal), bit for bit:
+      * 2^20 random sums of squares, cols * 10^U(-30, 30): the fast path
+        must give at least 99.99 % of them;
+      * 2^20 sums whose result lies within about 2^-50 of an fp32 rounding
+        midpoint (x = 1 / m^2 for the midpoint m of two fp32 neighbours):
+        the fast path must decline almost all of them, so the fallback runs;
+      * zero (with eps = 0: infinity), and sums at the ends of the range."""
+    L = _probe()
+    rng = np.random.default_rng(cols)
+    n = 1 << 20
+    e64 = np.float64(np.float32(eps))
+    ss_rand = cols * 10.0 ** rng.uniform(-30, 30, n)
+    f = (2.0 ** rng.uniform(-40, 40, n)).astype(np.float32)
+    m = (f.astype(np.float64) + np.nextafter(f, np.float32(np.inf)).astype(np.float64)) / 2
+    ss_mid = (1.0 / (m * m) - e64) * cols
+    ss_mid = ss_mid[ss_mid > 0]
+    special = np.array([0.0, 2.0 ** -1000, 2.0 ** -266, 1.0, float(cols), 2.0 ** 600, 1e300], np.float64)
+    print(f"case inverse RMS cols={cols} eps={eps}", flush=True)
+    for name, ss in (("random", ss_rand), ("midpoint", ss_mid), ("special", special)):
+        st = torch.from_numpy(np.ascontiguousarray(ss)).cuda()
+        inv = torch.empty(ss.size, dtype=torch.float32, device="cuda")
+        fast = torch.empty(ss.size, dtype=torch.uint8, device="cuda")
+        rc = L.afqp_inv_rms(st.data_ptr(), cols, eps, inv.data_ptr(), fast.data_ptr(), ss.size, _stream())
+        assert rc == 0, rc
+        torch.cuda.synchronize()
+        got, fast = inv.cpu().numpy(), fast.cpu().numpy().astype(bool)
+        with np.errstate(divide="ignore", over="ignore"):   # 1/sqrt(0), results beyond fp32
+            want = (1.0 / np.sqrt(ss / np.float64(cols) + e64)).astype(np.float32)
+        bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+        assert bad.size == 0, (name, [(float(ss[i]), float(got[i]), float(want[i])) for i in bad[:5]])
+        share = float(fast.mean())
+        print(f"[sweep] inverse RMS {name}: {ss.size} values, fast path {share:.6f}", flush=True)
+        if name == "random":
+            assert share >= 0.9999
+        elif name == "midpoint":
+            assert share <= 0.01

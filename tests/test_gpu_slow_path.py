@@ -18,7 +18,7 @@ import torch
 import activation_fp8_quant_amd as afq
 import oracle as orc
 from activation_fp8_quant_amd import inputs
-from tests._gpu import HOST_THREADS, MODE, check_norm, dev16, host8, ref_norm, run_norm, scales_u8_or_f32
+from tests._gpu import HOST_THREADS, MODE, check_norm, dev16, host8, host16, ref_norm, run_norm, scales_u8_or_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -105,12 +105,13 @@ def test_quant_tiny_amax_around_both_boundaries(dtype, mode, width):
 
 @pytest.mark.parametrize("qin", [0, 1])
 @pytest.mark.parametrize("mode", ["b128", "pt"])
-@pytest.mark.parametrize("M,H", [(64, 4096), (300, 4096), (9, 2048)])
+@pytest.mark.parametrize("M,H", [(64, 4096), (300, 4096), (9, 2048), (300, 2048), (300, 1024)])
 def test_norm_tiny_weights_slow_path(qin, mode, M, H):
     """Standard RMSNorm whose weights are U(0.5, 1.5) * 2^k (k = -85,
     -118, -119, -120, -124): the normed rows are tiny, so group maxima fall
     on both sides of 2^-83, of 2^-116 and of 448 * 2^-126 and below; 1x128
-    and per-token, at decode and bandwidth row shapes, the default and the
+    and per-token, at decode and bandwidth row shapes (per-token rows of
+    2048 and 1024 at 300 rows run one wavefront a row), the default and the
     fp32-direct quantiser input.  Against the oracle within the contract
     (fp32-direct: bit-exact)."""
     d = inputs.norm_inputs(M, H, seed=62, x_std=1.0, r_std=1.0, w_kind="uniform", w_param=0.5)
@@ -126,3 +127,29 @@ def test_norm_tiny_weights_slow_path(qin, mode, M, H):
         seen_slow += int(((s > 0) & (s < np.float32(BOUND_FAST / 448))).sum())
         seen_sub += int(((s > 0) & (s < np.float32(2.0 ** -126))).sum())
     assert seen_slow > 0 and seen_sub > 0
+
+
+@pytest.mark.parametrize("M", [8, 300])
+@pytest.mark.parametrize("tiny", [0, 1])
+def test_two_segments_one_on_the_slow_path(M, tiny):
+    """Two per-token segments (1536 + 512) where one segment's weights are
+    scaled by 2^-120 (its scale on the slow path) and the
+    other's are not: the per-row choice between the fast and the slow
+    quantiser must follow each segment.  8 rows (multi-wavefront kernel)
+    and 300 rows (one wavefront a row); against the oracle."""
+    segs = inputs.two_segment_inputs(M, (1536, 512), seed=63)
+    w = inputs.bits_to_float(segs[tiny]["w"], "bf16").astype(np.float64)
+    segs[tiny]["w"] = inputs.to_bits(w * 2.0 ** -120)
+    print(f"case two segments, segment {tiny} tiny, M={M}", flush=True)
+    outs = afq.fused_add_rmsnorm_quant([dev16(sg["x"]) for sg in segs], [dev16(sg["w"]) for sg in segs], 1e-6,
+                                       mode=afq.PER_TOKEN, kind=afq.STANDARD, want_normed=True)
+    torch.cuda.synchronize()
+    for j, (sg, qa) in enumerate(zip(segs, outs)):
+        gpu = dict(normed=host16(qa.normed), values=host8(qa.values), scales=scales_u8_or_f32(qa.scales))
+        ref = ref_norm(sg["x"], sg["w"], kind="standard", mode="pt")
+        check_norm(gpu, ref, "pt", "bf16", f"two-seg tiny={tiny} seg {j} M={M}")
+        s = np.asarray(ref["scales"], np.float32).ravel()
+        if j == tiny:
+            assert bool((s < np.float32(BOUND_FAST / 448)).all())
+        else:
+            assert bool((s >= np.float32(BOUND_FAST / 448)).all())
