@@ -95,15 +95,15 @@ __device__ __forceinline__ void silu_bf16x8(const float (&g)[8], const uint4 &gb
 {
     float raw[8];
     uint32_t dmin = 0xFFFFFFFFu; // (low 16 bits) - (0x8000 - 3): <= 6 when within 3 ulps of a midpoint
-    float gmin = g[0];
+    uint32_t gmax = 0u;          // largest gate bit pattern: above that of -80 for a gate below -80
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         raw[i] = s[i] = silu_fast(g[i]);
         dmin = min(dmin, (__float_as_uint(raw[i]) & 0xFFFFu) - (0x8000u - 3u));
-        gmin = __builtin_fminf(gmin, g[i]);
+        gmax = max(gmax, __float_as_uint(g[i]));
     }
     round8<kBF16>(s);
-    if (__builtin_expect(dmin <= 6u || gmin < -80.0f, 0)) {
+    if (__builtin_expect(dmin <= 6u || gmax > 0xC2A00000u, 0)) {
         const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -120,13 +120,13 @@ __device__ __forceinline__ void silu_bf16x8(const float (&g)[8], const uint4 &gb
 template <int N>
 __device__ __forceinline__ void silu_f32xn(const float (&g)[N], float (&s)[N])
 {
-    float gmin = g[0];
+    uint32_t gmax = 0u; // largest gate bit pattern: above that of -80 for a gate below -80
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         s[i] = silu_fast(g[i]);
-        gmin = __builtin_fminf(gmin, g[i]);
+        gmax = max(gmax, __float_as_uint(g[i]));
     }
-    if (gmin < -80.0f) {
+    if (gmax > 0xC2A00000u) {
 #pragma unroll 1
         for (int i = 0; i < N; ++i)
             if (g[i] < -80.0f) s[i] = silu_f32_slow(g[i]);
@@ -207,22 +207,23 @@ __device__ __forceinline__ uint2 pack4(const float (&v)[4])
     return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
-// The 1x128 outputs of one chunk from s = bf16(silu(gate)) and the up
-// values v (fp32, overwritten): a = bf16(s * up), the group scale
-// amax|a| / 448 over the 16 lanes of the group, the codes, and the
-// optional bf16 copy of a.
-__device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8], float (&v)[8],
-                                          int64_t r, int32_t lc)
+// The 1x128 outputs of chunk f (the launch's flat chunk index) from
+// s = bf16(silu(gate)) and the up values v (fp32, overwritten):
+// a = bf16(s * up), the group scale amax|a| / 448 over the 16 lanes of the
+// group, the codes, and the optional bf16 copy of a.  The outputs are dense
+// [rows, I] (codes, copy) and [rows, I / 128] (scales), and a row has a
+// multiple of 16 chunks, so chunk f's codes start at element 8 f and its
+// group's scale is entry f / 16: no row index is needed.
+__device__ __forceinline__ void b128_tail(const ActArgs &a, const float (&s)[8], float (&v)[8], uint32_t f)
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= s[i];
     const uint4 ap = round8<kBF16>(v);
-    const int64_t out_off = r * a.I + (int64_t)lc * 8;
+    const int64_t out_off = (int64_t)f * 8;
     if (a.act) stg_stream(a.act + out_off * 2, ap);
     const Fp32Scale sc = fp32_scale(max_row16(amax8(v)));
     const uint2 q = fp32scale_codes8(v, sc);
-    if ((lc & 15) == 0)
-        reinterpret_cast<float *>(a.scales)[r * (a.I / 128) + lc / 16] = sc.s;
+    if ((f & 15u) == 0) reinterpret_cast<float *>(a.scales)[f >> 4] = sc.s;
     stg_stream(a.values + out_off, q);
 }
 
@@ -239,17 +240,17 @@ act_quant_kernel(const ActArgs a)
     const uint32_t base = blockIdx.x * (256u * CPL) + threadIdx.x;
     uint4 gv[CPL], uv[CPL];
     bool ok[CPL];
-    int64_t rw[CPL];
-    int32_t lc[CPL];
+    // outputs are dense rows of C chunks: chunk f's outputs sit at f alone
+    // (element 8 f, MX scale f / 4); only the input, whose rows have a
+    // pitch, needs f's row and column
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const uint32_t f = base + k * 256u;
         ok[k] = f < a.total;
-        const uint32_t r = div_c(f, a.dc);
-        rw[k] = r;
-        lc[k] = (int32_t)(f - r * (uint32_t)a.C);
         if (ok[k]) {
-            const uint8_t *p = a.gu + rw[k] * a.gu_pitch + (int64_t)lc[k] * 16;
+            const uint32_t r = div_c(f, a.dc);
+            const int32_t lc = (int32_t)(f - r * (uint32_t)a.C);
+            const uint8_t *p = a.gu + (int64_t)r * a.gu_pitch + (int64_t)lc * 16;
             gv[k] = ldg_stream(p);
             uv[k] = ldg_stream(p + (int64_t)a.I * 2);
         }
@@ -257,12 +258,13 @@ act_quant_kernel(const ActArgs a)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue; // uniform over every quant group
+        const uint32_t f = base + k * 256u;
+        const int64_t out_off = (int64_t)f * 8;
         float g[8], v[8];
         unpack8<kBF16>(gv[k], g);
         unpack8<kBF16>(uv[k], v);
         if constexpr (!QUANT) {
             // the unfused SiLU-and-mul: the activation alone
-            const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
             if constexpr (MODE == kMX) {
                 act_f32xn<ACT, 8>(a, g, v);
             } else {
@@ -273,19 +275,18 @@ act_quant_kernel(const ActArgs a)
             }
             stg_stream(a.act + out_off * 2, pack8<kBF16>(v));
         } else if constexpr (MODE == kMX) {
-            const int64_t out_off = rw[k] * a.I + (int64_t)lc[k] * 8;
             uint2 q;
             act_f32xn<ACT, 8>(a, g, v);
             const uint4 ap = QBF16 ? round8<kBF16>(v) : pack8<kBF16>(v);
             if (a.act) stg_stream(a.act + out_off * 2, ap);
             const uint32_t b = e8m0_of(max_quad(amax8(v)));
             q = mx_codes8(v, mx_inv_scale(b));
-            if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.I / 32) + lc[k] / 4] = (uint8_t)b;
+            if ((f & 3u) == 0) a.scales[f >> 2] = (uint8_t)b;
             stg_stream(a.values + out_off, q);
         } else {
             float sg[8];
             silu_bf16x8(g, gv[k], sg);
-            b128_tail(a, sg, v, rw[k], lc[k]);
+            b128_tail(a, sg, v, f);
         }
     }
 }
@@ -323,10 +324,12 @@ act_mx4_kernel(const ActArgs a)
     const uint32_t b = e8m0_of(max_oct(__builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
                                                        __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])))));
     const float ix = mx_inv_scale(b);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[0] * ix), clamp448(v[1] * ix), 0, false);
+    const float q0 = clamp448(v[0] * ix);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, clamp448(v[1] * ix), __float_as_int(q0), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[2] * ix), clamp448(v[3] * ix), w, true);
-    if ((lc & 7) == 0) a.scales[(int64_t)r * (a.I / 32) + lc / 8] = (uint8_t)b;
-    stg_stream(a.values + (int64_t)r * a.I + (int64_t)lc * 4, (uint32_t)w);
+    // dense outputs: chunk f's codes at element 4 f, its block's scale at f / 8
+    if ((f & 7u) == 0) a.scales[f >> 3] = (uint8_t)b;
+    stg_stream(a.values + (int64_t)f * 4, (uint32_t)w);
 }
 
 // ================================================================ launcher

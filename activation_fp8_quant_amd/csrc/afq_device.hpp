@@ -460,8 +460,9 @@ __device__ __forceinline__ float quotient_fast(float u, const Fp32Scale &sc)
 // are at most 448(1+2^-23) in magnitude, which v_cvt_pk_fp8_f32 rounds to
 // 448 exactly as it rounds the clamped value (checked on the GPU over every
 // fp32 in [448, 464] of either sign), so no clamp is applied.  Other scales
-// take the IEEE division and the clamp; a zero scale gives zero codes.  The
-// choice is made once per chunk (it is uniform over a group).
+// take the IEEE division and the clamp; a zero scale gives zero codes (a
+// select after the conversion, of whatever the division gave).  The choice
+// is made once per chunk (it is uniform over a group).
 __device__ __forceinline__ uint2 fp32scale_codes8(const float (&u)[8], const Fp32Scale &sc)
 {
     float v[8];
@@ -472,8 +473,8 @@ __device__ __forceinline__ uint2 fp32scale_codes8(const float (&u)[8], const Fp3
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = clamp448(__builtin_copysignf(u[i] / sc.s, u[i]));
     }
-    if (sc.zero) return make_uint2(0u, 0u);
-    return cvt8_e4m3(v);
+    const uint2 q = cvt8_e4m3(v);
+    return make_uint2(sc.zero ? 0u : q.x, sc.zero ? 0u : q.y);
 }
 
 // ---------------------------------------------------------------- memory

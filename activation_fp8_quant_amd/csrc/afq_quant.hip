@@ -49,33 +49,35 @@ quant_flat_kernel(const QuantArgs a)
     const uint32_t base = blockIdx.x * (256u * CPL) + threadIdx.x;
     float v[CPL][8];
     bool ok[CPL];
-    int64_t rw[CPL];
-    int32_t lc[CPL];
+    // outputs are dense rows of C chunks (C a multiple of 4, of 16 for
+    // 1x128): chunk f's codes start at element 8 f and its group's scale is
+    // entry f / 4 (MX) or f / 16 (1x128); only the input, whose rows have a
+    // pitch, needs f's row and column
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const uint32_t f = base + k * 256u;
         ok[k] = f < a.total;
-        const uint32_t r = div_c(f, a.dc);
-        rw[k] = r;
-        lc[k] = (int32_t)(f - r * (uint32_t)a.C);
-        if (ok[k]) load_chunk<DT>(a.x + rw[k] * a.x_pitch + (int64_t)lc[k] * 8 * EB, v[k]);
+        if (ok[k]) {
+            const uint32_t r = div_c(f, a.dc);
+            const int32_t lc = (int32_t)(f - r * (uint32_t)a.C);
+            load_chunk<DT>(a.x + (int64_t)r * a.x_pitch + (int64_t)lc * 8 * EB, v[k]);
+        }
     }
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         if (!ok[k]) continue;
-        const int64_t out_off = rw[k] * a.cols + (int64_t)lc[k] * 8;
+        const uint32_t f = base + k * 256u;
         uint2 q;
         if constexpr (MODE == kMX) {
             const uint32_t b = e8m0_of(max_quad(amax8(v[k])));
             q = mx_codes8(v[k], mx_inv_scale(b));
-            if ((lc[k] & 3) == 0) a.scales[rw[k] * (a.cols / 32) + lc[k] / 4] = (uint8_t)b;
+            if ((f & 3u) == 0) a.scales[f >> 2] = (uint8_t)b;
         } else {
             const Fp32Scale sc = fp32_scale(max_row16(amax8(v[k])));
             q = fp32scale_codes8(v[k], sc);
-            if ((lc[k] & 15) == 0)
-                reinterpret_cast<float *>(a.scales)[rw[k] * (a.cols / 128) + lc[k] / 16] = sc.s;
+            if ((f & 15u) == 0) reinterpret_cast<float *>(a.scales)[f >> 4] = sc.s;
         }
-        stg_stream(a.values + out_off, q);
+        stg_stream(a.values + (int64_t)f * 8, q);
     }
 }
 
