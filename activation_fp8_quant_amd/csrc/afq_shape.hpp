@@ -88,10 +88,13 @@ static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 //  * per-token (two row reductions, each an LDS exchange across the row's
 //    wavefronts): up to 256 rows, rows of 256 to 512 lanes (two chunks per
 //    lane for rows wider than 2048; 7-23 % faster at widths 4096-8192, 8
-//    rows); above 256 rows, the fewest chunks per lane from two up whose
-//    row is a whole divisor of a CU's 32 wavefront slots (13-44 % faster
-//    than one chunk per lane from 512 rows: at width 6144, 4096 rows,
-//    27.6 -> 15.4 us at three chunks per lane);
+//    rows); above 256 rows, rows of 65 to 256 chunks on one wavefront
+//    (ceil(C / 64) chunks per lane: the kernel that keeps a row in one
+//    wavefront, with no LDS exchange; the two-segment 1536 + 512 launch at
+//    8192 rows 12.3 -> 11.4 us), and other rows the fewest chunks per lane
+//    from two up whose row is a whole divisor of a CU's 32 wavefront slots
+//    (13-44 % faster than one chunk per lane from 512 rows: at width 6144,
+//    4096 rows, 27.6 -> 15.4 us at three chunks per lane);
 //  * MXFP8 with the copy: when the base shape (one chunk per lane; two or
 //    more for rows wider than 1024 chunks) needs two or three rounds of
 //    rows, the fewest chunks per lane that hold every row in one round
@@ -108,7 +111,7 @@ static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool m
         if (M <= 256) {
             cpl = C > 256 ? 2 : 1;
         } else if (C > 64 && C <= 256) {
-            cpl = (C + 63) / 64; // one wavefront a row
+            cpl = (C + 63) / 64;
         } else {
             cpl = 2;
             for (int c = 2; c <= 4; ++c)

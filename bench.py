@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import threading
@@ -96,11 +97,22 @@ def _dev16(bits, dtype="bf16"):
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with runs of white space made one
+    space: what the compiler sees, so that a comment edit does not count as
+    a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def _src_hash():
+    """Hash of the norm kernel's sources (comments and layout excluded), to
+    tell whether stored counter figures still describe the kernel."""
     h = hashlib.sha256()
     for f in ("afq_norm.hip", "afq_device.hpp", "afq_launch.hpp", "afq_shape.hpp"):
-        with open(os.path.join(ROOT, "activation_fp8_quant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "activation_fp8_quant_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

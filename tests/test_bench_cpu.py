@@ -60,3 +60,14 @@ def test_copy_only_bytes():
     assert bench.silu_bytes(16384, 3072, quant=False) == 16384 * (2 * 2 * 3072 + 2 * 3072)
     # two segments without residual: x in, the copy out, both weights once
     assert bench.two_seg_bytes(8192, quant=False) == 8192 * 2 * 2 * 2048 + 2 * 2048
+
+
+def test_source_hash_ignores_comments_only():
+    """The hash that ties stored counter figures to the norm kernel's
+    sources sees code, not comments or layout."""
+    import bench
+    a = "int f(int x) { // one\n  return x + 1; /* two\n lines */ }\n"
+    b = "int f(int x) {\n\n    return x + 1;   }"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
