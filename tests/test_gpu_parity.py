@@ -1090,6 +1090,71 @@ def test_row_kernels_split_large_launches():
     torch.cuda.empty_cache()
 
 
+def _split_rows(M, step, base_rows, seed):
+    """Rows on both sides of each launch boundary (multiples of `step`),
+    the ends, and random rows; with their rows in the tiled base block."""
+    edge = [0, 1, M - 2, M - 1]
+    for b in range(step, M, step):
+        edge += [b - 2, b - 1, b, b + 1]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(seed).choice(M, 40, replace=False)]))
+    return rows, rows % base_rows
+
+
+def test_flat_kernels_split_large_launches():
+    """A flat launch keeps its chunk index below 2^31: more chunks take
+    several launches over row slices, each indexing its outputs from its
+    own first row.  The standalone quantiser (MXFP8 and 1x128 on rows of
+    256: 2^26 + 1000 rows, 32 GiB of input) and SiLU-and-mul (1x128 and
+    MXFP8 at I = 128: 2^27 + 1000 rows, 64 GiB of input), each input a
+    seeded 4096-row block tiled on the GPU; rows on both sides of the split
+    against the oracle on the block's rows, bit for bit (MXFP8 SiLU, whose
+    fp32 activation the contract holds to a budget: against the same rows
+    run as a small launch, bit for bit)."""
+    base_rows = 4096
+    # standalone quantiser: C = 32 chunks a row, 2^26 rows a launch
+    M = (1 << 26) + 1000
+    base = inputs.norm_inputs(base_rows, 256, seed=19, x_std=2.0, r_std=None, w_kind="uniform", w_param=0.5)["x"]
+    print(f"case flat split: fp8_quant on {M} rows of 256", flush=True)
+    x = dev16(base).repeat(M // base_rows + 1, 1)[:M]
+    rows, brow = _split_rows(M, 1 << 26, base_rows, 5)
+    idx = torch.from_numpy(rows).cuda()
+    for mode in (afq.MXFP8, afq.BLOCK128):
+        qa = afq.fp8_quant(x, mode)
+        torch.cuda.synchronize()
+        got_v = qa.values.view(torch.uint8)[idx].cpu().numpy()
+        got_s = qa.scales[idx].cpu().numpy()
+        del qa
+        q, sc = orc.quant(base[brow], orc.BF16, mode)
+        assert np.array_equal(got_v, q), mode
+        assert np.array_equal(np.ascontiguousarray(got_s).view(np.uint8), np.ascontiguousarray(sc).view(np.uint8)), mode
+    del x
+    torch.cuda.empty_cache()
+    # SiLU-and-mul: C = 16 chunks a row (I = 128), 2^27 rows a launch
+    M = (1 << 27) + 1000
+    base = inputs.gate_up_inputs(base_rows, 128, seed=20, std=2.0)
+    print(f"case flat split: silu_mul_quant on {M} rows of I=128", flush=True)
+    gu = dev16(base).repeat(M // base_rows + 1, 1)[:M]
+    rows, brow = _split_rows(M, 1 << 27, base_rows, 6)
+    idx = torch.from_numpy(rows).cuda()
+    for mode in (afq.BLOCK128, afq.MXFP8):
+        qa = afq.silu_mul_quant(gu, mode)
+        torch.cuda.synchronize()
+        got_v = qa.values.view(torch.uint8)[idx].cpu().numpy()
+        got_s = qa.scales[idx].cpu().numpy()
+        del qa
+        if mode == afq.BLOCK128:   # bit-exact against the oracle
+            ref = orc.silu_quant(base[brow], mode, want_act=False)
+            assert np.array_equal(got_v, ref["values"])
+            assert np.array_equal(got_s.view(np.uint32), ref["scales"].view(np.uint32))
+        else:                      # the same rows as a small launch, bit for bit
+            small = afq.silu_mul_quant(dev16(base[brow]), mode)
+            torch.cuda.synchronize()
+            assert np.array_equal(got_v, host8(small.values))
+            assert np.array_equal(got_s, small.scales.cpu().numpy())
+    del gu
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------ full-size, every row
 @pytest.mark.parametrize("name,M,H,mode,normed", [
     ("headline add + Gemma RMSNorm + MXFP8 + copy", 16384, 6144, "mx", True),
