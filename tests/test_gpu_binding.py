@@ -82,3 +82,39 @@ def test_prepare_rejects_bad_use():
         afq.prepare(afq.fused_add_rmsnorm_quant, x, w, 1e-6, stream=torch.cuda.current_stream())
     with pytest.raises(ValueError):   # checked at prepare time, before any launch
         afq.prepare(afq.fused_add_rmsnorm_quant, x, w.cpu(), 1e-6)
+
+
+def test_prepared_launches_in_a_graph():
+    """Prepared launches (norm with residual and copy, SiLU-and-mul)
+    captured into a HIP graph on the capture stream, then replayed three
+    times with new input contents written in place between replays (and the
+    outputs poisoned): every replay equals the entry points' eager launches
+    on the same inputs.  The residual is not updated in place here, so each
+    replay starts from the same residual."""
+    d = inputs.norm_inputs(24, 4096, seed=52, x_std=3.0, r_std=1.0, w_kind="normal", w_param=0.1)
+    x, w, r = dev16(d["x"]), dev16(d["w"]), dev16(d["r"])
+    gu = dev16(inputs.gate_up_inputs(24, 768, seed=52, std=2.0))
+    kw = dict(mode=afq.MXFP8, kind=afq.GEMMA, residual=r, want_normed=True)
+    norm = afq.prepare(afq.fused_add_rmsnorm_quant, x, w, 1e-6, **kw)
+    silu = afq.prepare(afq.silu_mul_quant, gu, afq.BLOCK128)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            got_n = norm(stream=s)
+            got_s = silu(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        x.mul_(-0.75).add_(0.5)
+        gu.mul_(1.25)
+        for t in (got_n.values, got_n.scales, got_n.normed, got_n.residual, got_s.values, got_s.scales):
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(got_n, afq.fused_add_rmsnorm_quant(x, w, 1e-6, **kw))
+        _same(got_s, afq.silu_mul_quant(gu, afq.BLOCK128))
+        torch.cuda.synchronize()
