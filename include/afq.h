@@ -39,7 +39,9 @@
  *             q = e4m3(clamp(u * 2^(127-b), -448, 448))
  *   1x128 / per-token:
  *             s = fp32(amax|u| / 448);  q = e4m3(clamp(fp32(u / s), +-448))
- *             (an all-zero group stores s = 0 and codes 0x00)
+ *             (an all-zero group, and one whose amax / 448 rounds to zero
+ *             in fp32 -- amax <= 224 * 2^-149, reachable from fp32 rows
+ *             only -- stores s = 0 and codes 0x00)
  *   e4m3 rounding is round-to-nearest-even on OCP e4m3fn (max 448,
  *   subnormals k * 2^-9, sign in bit 7).
  * fp32-direct variant (quant_input = AFQ_QIN_FP32; 1x128 and per-token):
