@@ -870,7 +870,12 @@ int launch_norm(const NormPlan &p, void *stream)
     a.C = p.seg[0].chunks + (p.nseg > 1 ? p.seg[1].chunks : 0);
     const int mode = p.quant ? p.mode : kNone;
     const bool copy = p.seg[0].normed != nullptr || (p.nseg > 1 && p.seg[1].normed != nullptr);
-    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode == kPT, mode == kMX && copy, device_cus());
+    const bool f32q = p.qin == 1;
+    // per-token rows of up to 256 rows on one wavefront: when the
+    // one-wavefront kernel serves the launch (not the fp32-direct form) and
+    // the row has no residual or at most 128 chunks
+    const bool small_one_wave = mode == kPT && !f32q && (p.nseg > 1 || p.res_in == nullptr || a.C <= 128);
+    const RowShapeRt sh = norm_row_shape(a.C, p.M, mode == kPT, mode == kMX && copy, device_cus(), small_one_wave);
     a.NT = sh.NT;
     a.R = sh.R;
     a.WPR = sh.WPR;
@@ -881,7 +886,6 @@ int launch_norm(const NormPlan &p, void *stream)
     a.rcols1 = 1.0 / (double)(p.nseg > 1 ? p.seg[1].cols : p.seg[0].cols);
     hipStream_t st = (hipStream_t)stream;
     const bool gemma = p.kind == 1;
-    const bool f32q = p.qin == 1;
     // per-token rows on one wavefront at two to four chunks per lane: the
     // kernel without LDS or barrier (the fp32-direct form keeps the general
     // kernel, whose fp64 reduction it has)

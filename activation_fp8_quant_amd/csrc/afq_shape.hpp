@@ -86,15 +86,21 @@ static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 // The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
 // 2048 / 4096 / 6144 / 8192, 1 to 4096 rows, one to four chunks per lane):
 //  * per-token (two row reductions, each an LDS exchange across the row's
-//    wavefronts): up to 256 rows, rows of 256 to 512 lanes (two chunks per
-//    lane for rows wider than 2048; 7-23 % faster at widths 4096-8192, 8
-//    rows); above 256 rows, rows of 65 to 256 chunks on one wavefront
-//    (ceil(C / 64) chunks per lane: the kernel that keeps a row in one
-//    wavefront, with no LDS exchange; the two-segment 1536 + 512 launch at
-//    8192 rows 12.3 -> 11.4 us), and other rows the fewest chunks per lane
-//    from two up whose row is a whole divisor of a CU's 32 wavefront slots
-//    (13-44 % faster than one chunk per lane from 512 rows: at width 6144,
-//    4096 rows, 27.6 -> 15.4 us at three chunks per lane);
+//    wavefronts): rows of 65 to 256 chunks on one wavefront (ceil(C / 64)
+//    chunks per lane: the kernel that keeps a row in one wavefront, with no
+//    LDS exchange) above 256 rows, and up to 256 rows when `small_one_wave`
+//    says so (the launcher sets it when the one-wavefront kernel serves the
+//    launch and the row has no residual or at most 128 chunks: the
+//    two-segment 1536 + 512 launch at 8192 rows 12.3 -> 11.4 us, at 8 rows
+//    2.79 -> 2.67 us, width 1024 with the residual at 8 rows 2.51 -> 2.43
+//    us; with the residual at 192 to 256 chunks one wavefront's chain is
+//    the longer, width 2048 at 192 rows 2.75 -> 3.38 us); other rows up to
+//    256 rows on 256 to 512 lanes (two chunks per lane for rows wider than
+//    2048; 7-23 % faster at widths 4096-8192, 8 rows), above 256 rows the
+//    fewest chunks per lane from two up whose row is a whole divisor of a
+//    CU's 32 wavefront slots (13-44 % faster than one chunk per lane from
+//    512 rows: at width 6144, 4096 rows, 27.6 -> 15.4 us at three chunks
+//    per lane);
 //  * MXFP8 with the copy: when the base shape (one chunk per lane; two or
 //    more for rows wider than 1024 chunks) needs two or three rounds of
 //    rows, the fewest chunks per lane that hold every row in one round
@@ -104,14 +110,15 @@ static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 //    launch is bandwidth-bound and longer lane work only costs);
 //  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
 //    per lane, which the same sweep found best for 1x128 at every size.
-static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool mx_copy, int64_t cus)
+static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool mx_copy, int64_t cus,
+                                        bool small_one_wave)
 {
     int cpl = 1;
     if (per_token) {
-        if (M <= 256) {
-            cpl = C > 256 ? 2 : 1;
-        } else if (C > 64 && C <= 256) {
+        if (C > 64 && C <= 256 && (M > 256 || small_one_wave)) {
             cpl = (C + 63) / 64;
+        } else if (M <= 256) {
+            cpl = C > 256 ? 2 : 1;
         } else {
             cpl = 2;
             for (int c = 2; c <= 4; ++c)

@@ -87,9 +87,13 @@ int main()
                 ++shapes;
             }
             for (long long cus : cuss)
-                for (int v = 0; v < 3; ++v) { // per-token, MXFP8 with the copy, anything else
-                    const RowShapeRt s = norm_row_shape(C, M, v == 0, v == 1, cus);
-                    check_shape(s, C, v == 0 ? "norm pt" : v == 1 ? "norm mx copy" : "norm other", M, cus);
+                for (int v = 0; v < 4; ++v) { // per-token, MXFP8 with the copy, anything else, per-token
+                                              // without one wavefront a row at up to 256 rows
+                    const bool pt = v == 0 || v == 3;
+                    const RowShapeRt s = norm_row_shape(C, M, pt, v == 1, cus, v != 3);
+                    check_shape(s, C, pt ? "norm pt" : v == 1 ? "norm mx copy" : "norm other", M, cus);
+                    if (pt && C > 64 && C <= 256 && (M > 256 || v == 0))
+                        CHECK(s.WPR == 1 && s.CPL == (C + 63) / 64, "pt one wavefront C=%d M=%lld", C, M);
                     if (v == 2) expect(s, shape_at(C, 1).NT, shape_at(C, 1).CPL, shape_at(C, 1).R, "norm other");
                     const int base = shape_at(C, 1).CPL;
                     if (v == 1 && s.CPL > base) { // only taken when it holds every row in one round
@@ -97,7 +101,7 @@ int main()
                         CHECK(M > norm_rows_per_round(C, base, cus) && M <= 3 * norm_rows_per_round(C, base, cus),
                               "mx copy C=%d M=%lld CPL=%d", C, M, s.CPL);
                     }
-                    if (v == 0 && M > 256) // per-token: whole rows fill a CU's 32 slots where some shape can
+                    if (pt && M > 256) // per-token: whole rows fill a CU's 32 slots where some shape can
                         CHECK(32 % s.WPR == 0 || (32 % shape_at(C, 2).WPR && 32 % shape_at(C, 3).WPR &&
                                                   32 % shape_at(C, 4).WPR),
                               "pt C=%d M=%lld WPR=%d", C, M, s.WPR);
@@ -109,24 +113,30 @@ int main()
     }
 
     // The rule's picks at the sizes it was measured on (256 compute units).
-    expect(norm_row_shape(768, 16384, false, true, 256), 768, 1, 1, "width 6144, 16384 rows, MXFP8 + copy");
-    expect(norm_row_shape(768, 512, false, true, 256), 768, 1, 1, "width 6144, 512 rows (one round)");
-    expect(norm_row_shape(768, 1024, false, true, 256), 384, 2, 1, "width 6144, 1024 rows, MXFP8 + copy");
-    expect(norm_row_shape(768, 1536, false, true, 256), 256, 3, 1, "width 6144, 1536 rows, MXFP8 + copy");
-    expect(norm_row_shape(768, 1537, false, true, 256), 768, 1, 1, "width 6144, 1537 rows (four rounds)");
-    expect(norm_row_shape(512, 3072, false, true, 256), 128, 4, 2, "width 4096, 3072 rows, MXFP8 + copy");
-    expect(norm_row_shape(768, 1024, false, false, 256), 768, 1, 1, "width 6144, 1024 rows, 1x128");
-    expect(norm_row_shape(768, 8, true, false, 256), 384, 2, 1, "width 6144, 8 rows, per-token");
-    expect(norm_row_shape(256, 8, true, false, 256), 256, 1, 1, "width 2048, 8 rows, per-token");
-    expect(norm_row_shape(768, 4096, true, false, 256), 256, 3, 1, "width 6144, 4096 rows, per-token");
-    expect(norm_row_shape(1024, 300, true, false, 256), 512, 2, 1, "width 8192, 300 rows, per-token");
-    expect(norm_row_shape(96, 8, true, false, 256), 128, 1, 2, "width 768, 8 rows, per-token");
-    expect(norm_row_shape(4096, 8, true, false, 256), 1024, 4, 1, "width 32768, 8 rows, per-token");
+    expect(norm_row_shape(768, 16384, false, true, 256, false), 768, 1, 1, "width 6144, 16384 rows, MXFP8 + copy");
+    expect(norm_row_shape(768, 512, false, true, 256, false), 768, 1, 1, "width 6144, 512 rows (one round)");
+    expect(norm_row_shape(768, 1024, false, true, 256, false), 384, 2, 1, "width 6144, 1024 rows, MXFP8 + copy");
+    expect(norm_row_shape(768, 1536, false, true, 256, false), 256, 3, 1, "width 6144, 1536 rows, MXFP8 + copy");
+    expect(norm_row_shape(768, 1537, false, true, 256, false), 768, 1, 1, "width 6144, 1537 rows (four rounds)");
+    expect(norm_row_shape(512, 3072, false, true, 256, false), 128, 4, 2, "width 4096, 3072 rows, MXFP8 + copy");
+    expect(norm_row_shape(768, 1024, false, false, 256, false), 768, 1, 1, "width 6144, 1024 rows, 1x128");
+    expect(norm_row_shape(768, 8, true, false, 256, true), 384, 2, 1, "width 6144, 8 rows, per-token");
+    expect(norm_row_shape(256, 8, true, false, 256, true), 64, 4, 4, "width 2048, 8 rows, per-token (one wavefront a row)");
+    expect(norm_row_shape(256, 8192, true, false, 256, true), 64, 4, 4, "width 2048, 8192 rows, per-token (one wavefront a row)");
+    expect(norm_row_shape(65, 1, true, false, 256, true), 64, 2, 4, "width 520, 1 row, per-token (one wavefront a row)");
+    expect(norm_row_shape(64, 300, true, false, 256, true), 64, 1, 4, "width 512, 300 rows, per-token (one chunk per lane)");
+    expect(norm_row_shape(768, 4096, true, false, 256, true), 256, 3, 1, "width 6144, 4096 rows, per-token");
+    expect(norm_row_shape(1024, 300, true, false, 256, true), 512, 2, 1, "width 8192, 300 rows, per-token");
+    expect(norm_row_shape(96, 8, true, false, 256, true), 64, 2, 4, "width 768, 8 rows, per-token (one wavefront a row)");
+    expect(norm_row_shape(96, 8, true, false, 256, false), 128, 1, 2, "width 768, 8 rows, per-token (multi-wavefront)");
+    expect(norm_row_shape(256, 192, true, false, 256, false), 256, 1, 1, "width 2048, 192 rows, per-token (multi-wavefront)");
+    expect(norm_row_shape(256, 300, true, false, 256, false), 64, 4, 4, "width 2048, 300 rows, per-token (one wavefront a row)");
+    expect(norm_row_shape(4096, 8, true, false, 256, true), 1024, 4, 1, "width 32768, 8 rows, per-token");
     // rows wider than 1024 chunks: rounds counted on the shapes that run
-    expect(norm_row_shape(2048, 600, false, true, 256), 512, 4, 1, "width 16384, 600 rows, MXFP8 + copy");
-    expect(norm_row_shape(2048, 1000, false, true, 256), 1024, 2, 1, "width 16384, 1000 rows (two rounds at four)");
-    expect(norm_row_shape(1025, 300, false, true, 256), 576, 2, 1, "width 8200, 300 rows (one round)");
-    expect(norm_row_shape(1025, 1000, false, true, 256), 384, 3, 1, "width 8200, 1000 rows, MXFP8 + copy");
+    expect(norm_row_shape(2048, 600, false, true, 256, false), 512, 4, 1, "width 16384, 600 rows, MXFP8 + copy");
+    expect(norm_row_shape(2048, 1000, false, true, 256, false), 1024, 2, 1, "width 16384, 1000 rows (two rounds at four)");
+    expect(norm_row_shape(1025, 300, false, true, 256, false), 576, 2, 1, "width 8200, 300 rows (one round)");
+    expect(norm_row_shape(1025, 1000, false, true, 256, false), 384, 3, 1, "width 8200, 1000 rows, MXFP8 + copy");
     // the standalone per-token quantiser at the sizes it was measured on
     expect(quant_row_shape(1024, 8, 256), 512, 2, 1, "quant width 8192, 8 rows");
     expect(quant_row_shape(1024, 1024, 256), 512, 2, 1, "quant width 8192, 1024 rows (one round at two)");

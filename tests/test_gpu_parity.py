@@ -265,11 +265,13 @@ def test_two_segment_unaligned_boundary(mode, widths, qin, M):
 @pytest.mark.parametrize("widths,dtype", [((1536, 512), "bf16"), ((1536, 512), "fp16"), ((512, 1536), "bf16"),
                                           ((1024, 1024), "bf16"), ((1000, 512), "bf16"), ((8, 2040), "bf16")])
 def test_two_segment_rows_independent_of_launch_shape(widths, dtype):
-    """Two per-token segments: 8 rows run on the multi-wavefront kernel (one
-    chunk per lane), 300 and 1100 rows on one wavefront a row, with the
-    segment boundary in slot 3, 1 or 2 (1536 + 512, 512 + 1536, 1024 + 1024)
-    or inside a slot (1000 + 512, 8 + 2040).  The first 8 rows of every
-    launch are bit-identical (codes, scales, copy), and against the oracle."""
+    """Two per-token segments on one wavefront a row, with the segment
+    boundary in slot 3, 1 or 2 (1536 + 512, 512 + 1536, 1024 + 1024) or
+    inside a slot (1000 + 512, 8 + 2040), at 8, 300 and 1100 rows: the first
+    8 rows of every launch are bit-identical (codes, scales, copy), and
+    against the oracle; and their copy equals, bit for bit, the copy-only
+    launch of the same rows, which runs the multi-wavefront kernel (one
+    chunk per lane, the rows' sums of squares meeting in LDS)."""
     print(f"case two-seg shape invariance {widths} {dtype}", flush=True)
     segs = inputs.two_segment_inputs(1100, widths, seed=43, dtype=dtype)
     first = None
@@ -290,6 +292,13 @@ def test_two_segment_rows_independent_of_launch_shape(widths, dtype):
             for k in a:
                 assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), \
                     (widths, M, i, k)
+    xs = [dev16(sg["x"][:8], dtype) for sg in segs]
+    ws = [dev16(sg["w"], dtype) for sg in segs]
+    plain = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=afq.PER_TOKEN, kind=afq.STANDARD,
+                                        quantize=False)
+    torch.cuda.synchronize()
+    for i, (qa, b) in enumerate(zip(plain, first)):
+        assert np.array_equal(host16(qa.normed), b["normed"]), (widths, i)
 
 
 # ----------------------------------------------------------- SiLU-and-mul

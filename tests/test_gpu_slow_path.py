@@ -135,8 +135,8 @@ def test_two_segments_one_on_the_slow_path(M, tiny):
     """Two per-token segments (1536 + 512) where one segment's weights are
     scaled by 2^-120 (its scale on the slow path) and the
     other's are not: the per-row choice between the fast and the slow
-    quantiser must follow each segment.  8 rows (multi-wavefront kernel)
-    and 300 rows (one wavefront a row); against the oracle."""
+    quantiser must follow each segment, at 8 and 300 rows (one wavefront a
+    row); against the oracle."""
     segs = inputs.two_segment_inputs(M, (1536, 512), seed=63)
     w = inputs.bits_to_float(segs[tiny]["w"], "bf16").astype(np.float64)
     segs[tiny]["w"] = inputs.to_bits(w * 2.0 ** -120)
