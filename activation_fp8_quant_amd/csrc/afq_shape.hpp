@@ -83,6 +83,14 @@ static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
     return rows_per_round(C, cpl, shape_at(C, cpl).CPL >= 4 ? 28 : 32, cus);
 }
 
+// Whether M rows in the row shape s fill at most 90 % of the wavefront
+// slots of `cus` compute units (the norm kernel's 32 per CU, 28 at four
+// chunks per lane).
+static inline bool norm_round_has_room(const RowShapeRt &s, int64_t M, int64_t cus)
+{
+    return 10 * M * s.WPR <= 9 * cus * (s.CPL >= 4 ? 28 : 32);
+}
+
 // The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
 // 2048 / 4096 / 6144 / 8192, 1 to 4096 rows, one to four chunks per lane):
 //  * per-token (two row reductions, each an LDS exchange across the row's
@@ -101,13 +109,22 @@ static inline int64_t norm_rows_per_round(int C, int cpl, int64_t cus)
 //    CU's 32 wavefront slots (13-44 % faster than one chunk per lane from
 //    512 rows: at width 6144, 4096 rows, 27.6 -> 15.4 us at three chunks
 //    per lane);
-//  * MXFP8 with the copy: when the base shape (one chunk per lane; two or
-//    more for rows wider than 1024 chunks) needs two or three rounds of
-//    rows, the fewest chunks per lane that hold every row in one round
-//    (7-13 % faster: width 6144, 1024 rows 12.8 -> 11.3 us; width 4096,
-//    3072 rows 21.7 -> 20.2 us at four chunks per lane); one chunk per lane
-//    otherwise (at one round it is as fast, at four or more rounds the
-//    launch is bandwidth-bound and longer lane work only costs);
+//  * MXFP8 with the copy: the base shape (one chunk per lane; two or more
+//    for rows wider than 1024 chunks) when one round of it holds every row
+//    with at most 90 % of the GPU's wavefront slots filled; otherwise, up
+//    to three rounds of rows at the base shape, the fewest chunks per lane
+//    whose round does, shapes with no idle chunk slot (NT * CPL = C) first,
+//    then any.  A round that fills every slot is
+//    slow: width 2048 at 2048 rows 8.64 us at one chunk per lane, 7.83 at
+//    two; width 4096 at 1024 rows 8.60 -> 7.83; width 8192 at 1024 rows
+//    14.81 us at two, 14.15 at four.  Rounds left partly empty cost little
+//    (width 6144 at 512 rows, three quarters of the slots: one chunk per
+//    lane is the fastest).  Over a sweep of widths 2048 / 4096 / 6144 /
+//    7168 / 8192 at 256 to 4096 rows the rule is at most 2.5 % off the best
+//    shape of any launch (the rule it replaced, which went to more chunks
+//    per lane only above one round: 10.5 %).  Above three rounds one chunk
+//    per lane (the launch is bandwidth-bound, and longer lane work only
+//    costs);
 //  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
 //    per lane, which the same sweep found best for 1x128 at every size.
 static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool mx_copy, int64_t cus,
@@ -127,15 +144,14 @@ static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool m
                     break;
                 }
         }
-    } else if (mx_copy) {
-        const int base = shape_at(C, 1).CPL; // above one for rows wider than 1024 chunks
-        const int64_t r1 = norm_rows_per_round(C, base, cus);
-        if (M > r1 && M <= 3 * r1)
-            for (int c = base + 1; c <= 4; ++c)
-                if (norm_rows_per_round(C, c, cus) >= M) {
-                    cpl = c;
-                    break;
-                }
+    } else if (mx_copy && M <= 3 * norm_rows_per_round(C, 1, cus) &&
+               !(M <= norm_rows_per_round(C, 1, cus) && norm_round_has_room(shape_at(C, 1), M, cus))) {
+        for (int pass = 0; pass < 2; ++pass)
+            for (int c = 1; c <= 4; ++c) {
+                const RowShapeRt s = shape_at(C, c);
+                if (pass == 0 && s.NT * s.CPL != C) continue;
+                if (norm_rows_per_round(C, c, cus) >= M && norm_round_has_room(s, M, cus)) return s;
+            }
     }
     return shape_at(C, cpl);
 }

@@ -95,12 +95,17 @@ int main()
                     if (pt && C > 64 && C <= 256 && (M > 256 || v == 0))
                         CHECK(s.WPR == 1 && s.CPL == (C + 63) / 64, "pt one wavefront C=%d M=%lld", C, M);
                     if (v == 2) expect(s, shape_at(C, 1).NT, shape_at(C, 1).CPL, shape_at(C, 1).R, "norm other");
-                    const int base = shape_at(C, 1).CPL;
-                    if (v == 1 && s.CPL > base) { // only taken when it holds every row in one round
-                        CHECK(norm_rows_per_round(C, s.CPL, cus) >= M, "mx copy C=%d M=%lld CPL=%d", C, M, s.CPL);
-                        CHECK(M > norm_rows_per_round(C, base, cus) && M <= 3 * norm_rows_per_round(C, base, cus),
+                    const RowShapeRt b = shape_at(C, 1);
+                    if (v == 1 && s.CPL > b.CPL) { // only taken when it holds every row in one round
+                                                   // with room, and the base shape does not
+                        CHECK(norm_rows_per_round(C, s.CPL, cus) >= M && norm_round_has_room(s, M, cus),
+                              "mx copy C=%d M=%lld CPL=%d", C, M, s.CPL);
+                        CHECK(M <= 3 * norm_rows_per_round(C, 1, cus) &&
+                                  (M > norm_rows_per_round(C, 1, cus) || !norm_round_has_room(b, M, cus)),
                               "mx copy C=%d M=%lld CPL=%d", C, M, s.CPL);
                     }
+                    if (v == 1 && M <= norm_rows_per_round(C, 1, cus) && norm_round_has_room(b, M, cus))
+                        expect(s, b.NT, b.CPL, b.R, "mx copy, room at the base shape");
                     if (pt && M > 256) // per-token: whole rows fill a CU's 32 slots where some shape can
                         CHECK(32 % s.WPR == 0 || (32 % shape_at(C, 2).WPR && 32 % shape_at(C, 3).WPR &&
                                                   32 % shape_at(C, 4).WPR),
@@ -119,6 +124,15 @@ int main()
     expect(norm_row_shape(768, 1536, false, true, 256, false), 256, 3, 1, "width 6144, 1536 rows, MXFP8 + copy");
     expect(norm_row_shape(768, 1537, false, true, 256, false), 768, 1, 1, "width 6144, 1537 rows (four rounds)");
     expect(norm_row_shape(512, 3072, false, true, 256, false), 128, 4, 2, "width 4096, 3072 rows, MXFP8 + copy");
+    expect(norm_row_shape(256, 2048, false, true, 256, false), 128, 2, 2, "width 2048, 2048 rows (a full round at one)");
+    expect(norm_row_shape(512, 1024, false, true, 256, false), 256, 2, 1, "width 4096, 1024 rows (a full round at one)");
+    expect(norm_row_shape(1024, 512, false, true, 256, false), 512, 2, 1, "width 8192, 512 rows (a full round at one)");
+    expect(norm_row_shape(512, 2048, false, true, 256, false), 128, 4, 2, "width 4096, 2048 rows (a full round at two)");
+    expect(norm_row_shape(1024, 1024, false, true, 256, false), 256, 4, 1, "width 8192, 1024 rows (a full round at two)");
+    expect(norm_row_shape(896, 1536, false, true, 256, false), 256, 4, 1, "width 7168, 1536 rows, MXFP8 + copy");
+    expect(norm_row_shape(896, 512, false, true, 256, false), 896, 1, 1, "width 7168, 512 rows (room at one)");
+    expect(norm_row_shape(256, 2047, false, true, 256, false), 128, 2, 2, "width 2048, 2047 rows (over 90 % of the slots)");
+    expect(norm_row_shape(256, 1843, false, true, 256, false), 256, 1, 1, "width 2048, 1843 rows (room at one)");
     expect(norm_row_shape(768, 1024, false, false, 256, false), 768, 1, 1, "width 6144, 1024 rows, 1x128");
     expect(norm_row_shape(768, 8, true, false, 256, true), 384, 2, 1, "width 6144, 8 rows, per-token");
     expect(norm_row_shape(256, 8, true, false, 256, true), 64, 4, 4, "width 2048, 8 rows, per-token (one wavefront a row)");
