@@ -345,6 +345,38 @@ def test_silu_b128_all_gates_exact():
     assert np.array_equal(gpu["values"], ref["values"])
 
 
+def test_silu_b128_flagged_gates_mixed_in_chunks():
+    """Chunks that mix the gates whose fast SiLU sits at a bf16 rounding
+    midpoint (5.9375, whose exact value the kernel holds as an immediate,
+    and 2^-7, -2^-8, odd subnormals, which it reads from the table), gates
+    below -80 (table) and ordinary gates, in every lane position of a chunk:
+    the activation bit-identical to the oracle."""
+    b = lambda v: int(inputs.to_bits(np.array([v]))[0])
+    special = [b(5.9375), b(2.0 ** -7), b(-(2.0 ** -8)), 0x0003, 0x8005, b(-100.0), b(-85.5)]
+    rng = np.random.default_rng(17)
+    rows = []
+    for _ in range(96):
+        g = inputs.to_bits(rng.normal(0.0, 3.0, 128))
+        for pos in rng.choice(128, size=rng.integers(1, 12), replace=False):
+            g[pos] = special[rng.integers(len(special))]
+        rows.append(g)
+    # and chunks of the midpoint gate alone, and with one other flagged gate
+    rows.append(np.full(128, special[0], np.uint16))
+    for other in special[1:]:
+        for lane in range(8):
+            g = np.full(128, special[0], np.uint16)
+            g[lane::8] = other
+            rows.append(g)
+    g = np.stack(rows).astype(np.uint16)
+    up = inputs.to_bits(rng.normal(0.0, 1.0, g.shape))
+    gu = np.concatenate([g, up], axis=1)
+    gpu = _run_silu(gu, "b128")
+    ref = orc.silu_quant(gu, orc.BLOCK128, threads=8)
+    check_dtype16(gpu["act"], ref["act"], "silu-b128 flagged act", exact=True)
+    assert np.array_equal(gpu["values"], ref["values"])
+    assert np.array_equal(gpu["scales"].view(np.uint32), ref["scales"].view(np.uint32))
+
+
 # Launches of at least this many chunks (8 activations each) are the
 # bandwidth-bound prefill sizes; their rows must equal the same rows run as
 # a small launch (batch invariance) as well as the oracle.
