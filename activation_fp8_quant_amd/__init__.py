@@ -203,6 +203,9 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+# the current device index without torch.cuda.current_device()'s wrapper
+# (the tensors are already on a device, so the runtime is initialised)
+_current_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
 
 
 def _stream(stream, dev: int) -> int:
@@ -370,7 +373,7 @@ def _call(fn, ref, stream, dev: int, what: str):
     """Call an entry point with the tensors' device current (HIP launches on
     the current device)."""
     arg = _stream(stream, dev)
-    if dev != torch.cuda.current_device():
+    if dev != _current_device():
         with torch.cuda.device(dev):
             st = fn(ref, arg)
     else:
