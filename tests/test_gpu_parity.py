@@ -134,6 +134,10 @@ def test_norm_bandwidth_row_counts(mode, H):
     ("mx", 4096, 3072, "bf16"),   # four chunks per lane, two rows of 128 lanes per block
     ("mx", 8192, 1536, "fp16"),   # four chunks per lane, 256 lanes
     ("mx", 2048, 3072, "bf16"),   # two chunks per lane, two rows per block
+    ("mx", 2048, 2048, "bf16"),   # a full round at one chunk per lane: two, two rows per block
+    ("mx", 8192, 512, "fp16"),    # a full round at one chunk per lane: two, 512 lanes
+    ("mx", 4096, 2048, "fp16"),   # a full round at two: four chunks per lane, two rows per block
+    ("mx", 7168, 1536, "bf16"),   # four chunks per lane on 256 lanes (128 idle chunk slots)
     ("pt", 6144, 300, "bf16"),    # above 256 rows: three chunks per lane
     ("pt", 8192, 64, "fp16"),     # up to 256 rows: two chunks per lane, 512 lanes
     ("pt", 2048, 257, "bf16"),    # two chunks per lane, two rows per block, a ragged block
@@ -143,8 +147,9 @@ def test_norm_bandwidth_row_counts(mode, H):
 ])
 def test_norm_row_shapes_by_size(mode, H, M, dtype):
     """The row shapes the launcher picks by row count (MXFP8 with the copy
-    at two or three rounds of rows; per-token at every size): every row
-    against the oracle, with the copy."""
+    wherever one round of the base shape cannot hold every row with room to
+    spare, up to three rounds; per-token at every size): every row against
+    the oracle, with the copy."""
     print(f"case row shape {mode} H={H} M={M} {dtype}", flush=True)
     d = inputs.norm_inputs(M, H, seed=13, x_std=2.0, r_std=1.0, w_kind="normal", w_param=0.1,
                            dtype=dtype)
