@@ -53,8 +53,9 @@ def _probe():
     L.afqp_e4m3_range.argtypes = [ctypes.c_uint32, P, I64, P]
     L.afqp_pack_bf16.argtypes = [P, P, I64, P]
     L.afqp_inv_rms.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, I64, P]
+    L.afqp_issue.argtypes = [ctypes.c_int, P, I64, ctypes.c_int32, P]
     for f in (L.afqp_scale, L.afqp_quotient, L.afqp_cvt8_e4m3, L.afqp_e4m3_range, L.afqp_pack_bf16,
-              L.afqp_inv_rms):
+              L.afqp_inv_rms, L.afqp_issue):
         f.restype = ctypes.c_int
     return L
 
@@ -272,3 +273,39 @@ def test_fp32_direct_inverse_rms(cols, eps):
             assert share >= 0.9999
         elif name == "midpoint":
             assert share <= 0.01
+
+
+# instruction kinds of the issue-rate probe, in its numbering, with the
+# independent chains each lane runs
+_ISSUE_KINDS = [("fp32 FMA", 8), ("exp2 (transcendental)", 8), ("rcp (transcendental)", 8),
+                ("v_cvt_pk_bf16_f32", 8), ("v_cvt_pk_fp8_f32", 8), ("v_bitop3_b32", 8),
+                ("integer add", 8), ("fp64 FMA", 4), ("v_dot2c_f32_bf16", 8)]
+
+
+def test_issue_rates():
+    """The issue rate of each instruction kind the kernels' arithmetic is
+    built from: a register-only kernel per kind (8 independent chains a lane,
+    4096 blocks of 256 lanes), timed by events, in cycles per wave64
+    instruction per SIMD at the nominal 2.4 GHz.  The figures are printed
+    (pytest -s shows them); the test asserts only that every kernel ran."""
+    L = _probe()
+    blocks, n = 4096, 4000
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert L.afqp_issue(0, out.data_ptr(), blocks, n, _stream()) == 0   # warm-up
+    torch.cuda.synchronize()
+    print(f"\nissue rates ({simds} SIMDs, 2.4 GHz nominal):", flush=True)
+    for op, (name, chains) in enumerate(_ISSUE_KINDS):
+        ms = []
+        for _ in range(3):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            rc = L.afqp_issue(op, out.data_ptr(), blocks, n, _stream())
+            e.record()
+            torch.cuda.synchronize()
+            assert rc == 0, (name, rc)
+            ms.append(s.elapsed_time(e))
+        t = sorted(ms)[1]
+        assert t > 0
+        cycles = t * 1e-3 * simds * 2.4e9 / (blocks * 4 * n * chains)
+        print(f"  {name:24s} {cycles:5.2f} cycles per wave64 instruction per SIMD", flush=True)
