@@ -307,6 +307,177 @@ def test_two_segment_rows_independent_of_launch_shape(widths, dtype):
 
 
 # ----------------------------------------------------------- SiLU-and-mul
+def _random_norm_configs(n, seed, budget=1.2e8):
+    """n seeded random norm launches: mode, kind, dtype, width (log-uniform
+    over 8-element chunks, a multiple of the group), row count (log-uniform
+    in 1 .. 6000), residual, copy, quantiser input and one or two segments;
+    at most `budget` elements in all, so the oracle runs in seconds."""
+    rng = np.random.default_rng(seed)
+    out, total = [], 0
+    while len(out) < n:
+        mode = str(rng.choice(["mx", "b128", "pt"]))
+        g = {"mx": 4, "b128": 16, "pt": 1}[mode]             # group in chunks
+        nseg = 2 if rng.random() < 0.25 else 1
+        widths = []
+        for _ in range(nseg):
+            c = int(np.exp(rng.uniform(0.0, np.log(4096 // nseg))))
+            widths.append(8 * max(g, c // g * g))
+        M = int(np.exp(rng.uniform(0.0, np.log(6000))))
+        elems = M * sum(widths)
+        if elems > 3e7 or total + elems > budget:
+            continue
+        total += elems
+        out.append(dict(mode=mode, widths=tuple(widths), M=M, kind=str(rng.choice(["gemma", "standard"])),
+                        dtype=str(rng.choice(["bf16", "fp16"])), res=nseg == 1 and rng.random() < 0.7,
+                        copy=bool(rng.random() < 0.7),
+                        qin=1 if mode != "mx" and rng.random() < 0.25 else 0, seed=int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_norm_configs(32, seed=20261203),
+                         ids=lambda c: f"{c['mode']}-{'+'.join(map(str, c['widths']))}-M{c['M']}-{c['kind']}-{c['dtype']}"
+                                       f"{'-res' if c['res'] else ''}{'-copy' if c['copy'] else ''}{'-f32q' if c['qin'] else ''}")
+def test_norm_random_configurations(cfg):
+    """Seeded random launches over every option of the norm (mode, kind,
+    dtype, width, row count, residual, copy, quantiser input, one or two
+    segments), so that the row-shape rules are reached at widths and row
+    counts no other test picks: every row against the oracle."""
+    print(f"case random norm {cfg}", flush=True)
+    mode, dtype, kind, qin = cfg["mode"], cfg["dtype"], cfg["kind"], cfg["qin"]
+    w_kind, w_param = ("normal", 0.1) if kind == "gemma" else ("uniform", 0.5)
+    if len(cfg["widths"]) == 1:
+        H = cfg["widths"][0]
+        d = inputs.norm_inputs(cfg["M"], H, seed=cfg["seed"], x_std=3.0, r_std=1.0 if cfg["res"] else None,
+                               w_kind=w_kind, w_param=w_param, dtype=dtype)
+        gpu = run_norm(d["x"], d["w"], r=d.get("r"), kind=kind, mode=mode, dtype=dtype,
+                       want_normed=cfg["copy"], qin=qin)
+        ref = ref_norm(d["x"], d["w"], r=d.get("r"), kind=kind, mode=mode, dtype=dtype, qin=qin)
+        check_norm(gpu, ref, mode, dtype, f"random {cfg}", requant=qin == 0, qin=qin)
+        return
+    segs = inputs.two_segment_inputs(cfg["M"], cfg["widths"], seed=cfg["seed"], dtype=dtype)
+    xs = [dev16(sg["x"], dtype) for sg in segs]
+    ws = [dev16(sg["w"], dtype) for sg in segs]
+    outs = afq.fused_add_rmsnorm_quant(xs, ws, 1e-6, mode=MODE[mode], kind=afq.GEMMA if kind == "gemma" else afq.STANDARD,
+                                       want_normed=cfg["copy"], quant_input=qin)
+    torch.cuda.synchronize()
+    for sg, qa in zip(segs, outs):
+        gpu = dict(normed=host16(qa.normed) if cfg["copy"] else None, values=host8(qa.values),
+                   scales=scales_u8_or_f32(qa.scales))
+        ref = ref_norm(sg["x"], sg["w"], kind=kind, mode=mode, dtype=dtype, qin=qin)
+        check_norm(gpu, ref, mode, dtype, f"random {cfg}", requant=qin == 0, qin=qin)
+
+
+def _random_act_configs(n, seed, budget=1.0e8):
+    """n seeded random activation launches: SiLU-and-mul in MXFP8 (with or
+    without the bf16 copy, the default or the bf16-first quantiser input)
+    or 1x128, or the clamped SwiGLU in MXFP8; width I log-uniform over
+    groups, rows log-uniform in 1 .. 6000, gate/up spread N(0, s^2) with s in
+    {1, 2, 3, 8}; at most `budget` activations in all."""
+    rng = np.random.default_rng(seed)
+    out, total = [], 0
+    while len(out) < n:
+        act = str(rng.choice(["silu", "silu", "swiglu"]))
+        mode = "mx" if act == "swiglu" else str(rng.choice(["mx", "b128"]))
+        g = 32 if mode == "mx" else 128
+        I = g * max(1, int(np.exp(rng.uniform(0.0, np.log(16384 // g)))))
+        M = int(np.exp(rng.uniform(0.0, np.log(6000))))
+        if M * I > 2e7 or total + M * I > budget:
+            continue
+        total += M * I
+        out.append(dict(act=act, mode=mode, I=I, M=M, std=float(rng.choice([1.0, 2.0, 3.0, 8.0])),
+                        copy=bool(rng.random() < 0.5), qin=2 if mode == "mx" and rng.random() < 0.3 else 0,
+                        seed=int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_act_configs(24, seed=20261204),
+                         ids=lambda c: f"{c['act']}-{c['mode']}-I{c['I']}-M{c['M']}-s{c['std']:g}"
+                                       f"{'-copy' if c['copy'] else ''}{'-bf16first' if c['qin'] else ''}")
+def test_activation_random_configurations(cfg):
+    """Seeded random SiLU-and-mul / clamped SwiGLU launches over mode, width,
+    row count, input spread, copy and quantiser input (so both forms of the
+    MXFP8 kernel, four values a lane and eight, are reached at widths no
+    other test picks): every row against the oracle, 1x128 bit-exact."""
+    print(f"case random activation {cfg}", flush=True)
+    gu = inputs.gate_up_inputs(cfg["M"], cfg["I"], seed=cfg["seed"], std=cfg["std"])
+    gt = dev16(gu)
+    if cfg["act"] == "swiglu":
+        qa = afq.swiglu_oai_quant(gt, 1.702, 1.0, 7.0, want_act=cfg["copy"], quant_input=cfg["qin"])
+        ref = orc.swiglu_oai_quant(gu, 1.702, 1.0, 7.0, orc.MXFP8, threads=HOST_THREADS, qin=cfg["qin"])
+    else:
+        qa = afq.silu_mul_quant(gt, MODE[cfg["mode"]], want_act=cfg["copy"], quant_input=cfg["qin"])
+        ref = orc.silu_quant(gu, MODE[cfg["mode"]], threads=HOST_THREADS, qin=cfg["qin"])
+    torch.cuda.synchronize()
+    values, scales = host8(qa.values), scales_u8_or_f32(qa.scales)
+    name = f"random {cfg}"
+    if cfg["mode"] == "b128":
+        assert np.array_equal(values, ref["values"]), name
+        assert np.array_equal(scales.view(np.uint32), ref["scales"].view(np.uint32)), name
+        if cfg["copy"]:
+            check_dtype16(host16(qa.normed), ref["act"], name + " act", exact=True)
+        return
+    check_codes(values, ref["values"], name)
+    check_scales(scales, ref["scales"], 0, name)
+    if cfg["copy"]:
+        check_dtype16(host16(qa.normed), ref["act"], name + " act")
+        if cfg["qin"] == 2:   # bf16-first: the fused codes are the quantiser's of the kernel's own copy
+            sep = afq.fp8_quant(qa.normed, afq.MXFP8)
+            torch.cuda.synchronize()
+            assert np.array_equal(values, host8(sep.values)), name
+            assert np.array_equal(scales, scales_u8_or_f32(sep.scales)), name
+
+
+def _random_quant_configs(n, seed, budget=1.0e8):
+    """n seeded random standalone quantiser launches: mode, input dtype
+    (bf16, fp16, fp32), width log-uniform over groups, rows log-uniform in
+    1 .. 6000, rows scaled by 2^k with k in [-40, 40]; at most `budget`
+    elements in all."""
+    rng = np.random.default_rng(seed)
+    out, total = [], 0
+    while len(out) < n:
+        mode = str(rng.choice(["mx", "b128", "pt"]))
+        g = {"mx": 32, "b128": 128, "pt": 8}[mode]
+        cols = g * max(1, int(np.exp(rng.uniform(0.0, np.log(32768 // g)))))
+        M = int(np.exp(rng.uniform(0.0, np.log(6000))))
+        if M * cols > 2e7 or total + M * cols > budget:
+            continue
+        total += M * cols
+        out.append(dict(mode=mode, dtype=str(rng.choice(["bf16", "fp16", "fp32"])), cols=cols, M=M,
+                        seed=int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_quant_configs(24, seed=20261205),
+                         ids=lambda c: f"{c['mode']}-{c['dtype']}-{c['cols']}-M{c['M']}")
+def test_fp8_quant_random_configurations(cfg):
+    """Seeded random standalone quantiser launches (every mode and input
+    dtype, widths up to 32768, row counts that reach each per-token row
+    shape, rows spread over 80 binades): codes and scales bit-exact."""
+    print(f"case random quant {cfg}", flush=True)
+    rng = np.random.default_rng(cfg["seed"])
+    M, n, dtype = cfg["M"], cfg["cols"], cfg["dtype"]
+    x = rng.standard_normal((M, n)) * 2.0 ** rng.integers(-40, 41, (M, 1))
+    if dtype == "fp16":
+        x = np.clip(x, -60000.0, 60000.0)
+    if dtype == "fp32":
+        xh = x.astype(np.float32)
+        xt = torch.from_numpy(xh).cuda()
+        odt = orc.FP32
+    else:
+        xh = inputs.to_bits(x, dtype)
+        xt = dev16(xh, dtype)
+        odt = ORC_DT[dtype]
+    qa = afq.fp8_quant(xt, MODE[cfg["mode"]])
+    torch.cuda.synchronize()
+    q, s = orc.quant(xh, odt, MODE[cfg["mode"]], threads=HOST_THREADS)
+    assert np.array_equal(host8(qa.values), q), cfg
+    gs = scales_u8_or_f32(qa.scales)
+    if cfg["mode"] == "mx":
+        assert np.array_equal(gs, s), cfg
+    else:
+        assert np.array_equal(gs.view(np.uint32), s.view(np.uint32)), cfg
+
+
 def _run_silu(gu, mode):
     qa = afq.silu_mul_quant(dev16(gu), MODE[mode], want_act=True)
     torch.cuda.synchronize()
