@@ -15,6 +15,12 @@
 //   afqp_pack_bf16 pack8<bf16> on 8 values at a time (v_cvt_pk_bf16_f32)
 //   afqp_inv_rms   inv_rms_f32q(ss, cols, RN64(1/cols), eps): the
 //                  fp32-direct inverse RMS, and which path gave it
+//   afqp_rows_pattern  the two-segment per-token norm's memory traffic
+//                  without its arithmetic: one wavefront a row, four 16-B
+//                  chunk loads a lane from a pitched row, a wavefront-wide
+//                  sum that every store waits for, 8-B stores to two dense
+//                  code arrays split at chunk C0 and a 4-B value a row and
+//                  segment
 //   afqp_issue     an issue-rate kernel: every lane runs 8 independent
 //                  chains of one instruction kind (fp32 FMA, exp2, rcp,
 //                  bf16 and e4m3 pair conversions, a three-input bitwise
@@ -98,6 +104,38 @@ int64_t grid_for(int64_t n)
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The two-segment per-token norm's access pattern (rows of C <= 256 chunks,
+// one wavefront each, four rows a 256-lane block): the same loads and
+// stores, with a wavefront-wide integer sum in place of the arithmetic.
+__global__ void __launch_bounds__(kBlock) k_rows_pattern(const uint8_t *x, int64_t pitch, uint8_t *q0, uint8_t *q1,
+                                                         float *s0, float *s1, int64_t M, int32_t C0, int32_t C)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return; // wavefront-uniform
+    uint4 v[4];
+    uint32_t acc = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = lane + 64 * k;
+        v[k] = c < C ? ldg_stream(x + row * pitch + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
+        acc += v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += (uint32_t)__shfl_xor((int)acc, off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = lane + 64 * k;
+        if (c >= C) continue;
+        const uint2 o = make_uint2(v[k].x ^ acc, v[k].z ^ acc);
+        if (c < C0) stg_stream(q0 + (row * C0 + c) * 8, o);
+        else stg_stream(q1 + (row * (C - C0) + (c - C0)) * 8, o);
+    }
+    if (lane == 0) {
+        s0[row] = __uint_as_float(acc & 0x3FFFFFFFu);
+        s1[row] = __uint_as_float(acc & 0x3FFFFFFFu);
+    }
+}
 
 // Issue-rate kernel OP: 8 independent chains a lane of one instruction kind
 // for n iterations, on registers only (the empty asm statements keep every
@@ -208,6 +246,23 @@ int afqp_pack_bf16(const float *v, uint16_t *out, int64_t n, void *stream)
     if (g < 0) return -1;
     if (g == 0) return 0;
     hipLaunchKernelGGL(k_pack_bf16, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, v, out, n / 8);
+    return (int)hipGetLastError();
+}
+
+// The two-segment per-token norm's memory pattern on M rows of C chunks
+// (0 < C0 <= C <= 256) read from x with a pitch of `pitch` bytes (a multiple
+// of 16); q0 holds M * C0 * 8 bytes, q1 M * (C - C0) * 8, s0 and s1 M floats.
+int afqp_rows_pattern(const uint8_t *x, int64_t pitch, uint8_t *q0, uint8_t *q1, float *s0, float *s1, int64_t M,
+                      int32_t C0, int32_t C, void *stream)
+{
+    if (M < 0 || C < 1 || C > 256 || C0 < 1 || C0 > C || pitch < (int64_t)C * 16 || pitch % 16 || !aligned16(x) ||
+        !q0 || (C0 < C && !q1) || !s0 || !s1)
+        return -1;
+    const int64_t g = (M + 3) / 4;
+    if (g > ((int64_t)1 << 31) - 1) return -1;
+    if (g == 0) return 0;
+    hipLaunchKernelGGL(k_rows_pattern, dim3((unsigned)g), dim3(kBlock), 0, (hipStream_t)stream, x, pitch, q0, q1, s0,
+                       s1, M, C0, C);
     return (int)hipGetLastError();
 }
 

@@ -54,8 +54,9 @@ def _probe():
     L.afqp_pack_bf16.argtypes = [P, P, I64, P]
     L.afqp_inv_rms.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, I64, P]
     L.afqp_issue.argtypes = [ctypes.c_int, P, I64, ctypes.c_int32, P]
+    L.afqp_rows_pattern.argtypes = [P, I64, P, P, P, P, I64, ctypes.c_int32, ctypes.c_int32, P]
     for f in (L.afqp_scale, L.afqp_quotient, L.afqp_cvt8_e4m3, L.afqp_e4m3_range, L.afqp_pack_bf16,
-              L.afqp_inv_rms, L.afqp_issue):
+              L.afqp_inv_rms, L.afqp_issue, L.afqp_rows_pattern):
         f.restype = ctypes.c_int
     return L
 
