@@ -91,8 +91,8 @@ static inline bool norm_round_has_room(const RowShapeRt &s, int64_t M, int64_t c
     return 10 * M * s.WPR <= 9 * cus * (s.CPL >= 4 ? 28 : 32);
 }
 
-// The norm kernel's row shape, chosen from a sweep (rotated buffers, widths
-// 2048 / 4096 / 6144 / 8192, 1 to 4096 rows, one to four chunks per lane):
+// The norm kernel's row shape, chosen from sweeps (rotated buffers, widths
+// 2048 to 8192, 1 to 4096 rows, one to four chunks per lane):
 //  * per-token (two row reductions, each an LDS exchange across the row's
 //    wavefronts): rows of 65 to 256 chunks on one wavefront (ceil(C / 64)
 //    chunks per lane: the kernel that keeps a row in one wavefront, with no
@@ -114,17 +114,19 @@ static inline bool norm_round_has_room(const RowShapeRt &s, int64_t M, int64_t c
 //    with at most 90 % of the GPU's wavefront slots filled; otherwise, up
 //    to three rounds of rows at the base shape, the fewest chunks per lane
 //    whose round does, shapes with no idle chunk slot (NT * CPL = C) first,
-//    then any.  A round that fills every slot is
-//    slow: width 2048 at 2048 rows 8.64 us at one chunk per lane, 7.83 at
-//    two; width 4096 at 1024 rows 8.60 -> 7.83; width 8192 at 1024 rows
-//    14.81 us at two, 14.15 at four.  Rounds left partly empty cost little
-//    (width 6144 at 512 rows, three quarters of the slots: one chunk per
-//    lane is the fastest).  Over a sweep of widths 2048 / 4096 / 6144 /
-//    7168 / 8192 at 256 to 4096 rows the rule is at most 2.5 % off the best
-//    shape of any launch (the rule it replaced, which went to more chunks
-//    per lane only above one round: 10.5 %).  Above three rounds one chunk
-//    per lane (the launch is bandwidth-bound, and longer lane work only
-//    costs);
+//    then any.  A round that fills every slot is slow: width 2048 at 2048
+//    rows 8.64 us at one chunk per lane, 7.83 at two; width 4096 at 1024
+//    rows 8.60 -> 7.83; width 8192 at 1024 rows 14.81 us at two, 14.15 at
+//    four.  Rounds left partly empty cost little (width 6144 at 512 rows,
+//    three quarters of the slots: one chunk per lane is the fastest).  Over
+//    a sweep of widths 2048 / 4096 / 6144 / 7168 / 8192 at 256 to 4096 rows
+//    the rule is at most 2.5 % off the best shape of any launch (the rule it
+//    replaced, which went to more chunks per lane only above one round:
+//    10.5 %), and at most 7.5 % at widths 3072 / 5120 / 10240 / 12288 /
+//    16384, which it was not fitted on.  At decode sizes (8 to 192 rows)
+//    one chunk per lane is the fastest by 0.1-0.7 us.  Above three rounds
+//    one chunk per lane (the launch is bandwidth-bound, and longer lane
+//    work only costs);
 //  * everything else (1x128, copy-only, MXFP8 without the copy): one chunk
 //    per lane, which the same sweep found best for 1x128 at every size.
 static inline RowShapeRt norm_row_shape(int C, int64_t M, bool per_token, bool mx_copy, int64_t cus,
