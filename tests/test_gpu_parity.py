@@ -314,7 +314,9 @@ def _random_norm_configs(n, seed, budget=1.2e8):
     at most `budget` elements in all, so the oracle runs in seconds."""
     rng = np.random.default_rng(seed)
     out, total = [], 0
-    while len(out) < n:
+    for _ in range(1_000_000):
+        if len(out) == n:
+            break
         mode = str(rng.choice(["mx", "b128", "pt"]))
         g = {"mx": 4, "b128": 16, "pt": 1}[mode]             # group in chunks
         nseg = 2 if rng.random() < 0.25 else 1
@@ -331,6 +333,8 @@ def _random_norm_configs(n, seed, budget=1.2e8):
                         dtype=str(rng.choice(["bf16", "fp16"])), res=nseg == 1 and rng.random() < 0.7,
                         copy=bool(rng.random() < 0.7),
                         qin=1 if mode != "mx" and rng.random() < 0.25 else 0, seed=int(rng.integers(1 << 30))))
+    if len(out) < n:
+        raise RuntimeError(f"{n} configurations do not fit a budget of {budget:g} elements")
     return out
 
 
@@ -375,7 +379,9 @@ def _random_act_configs(n, seed, budget=1.0e8):
     {1, 2, 3, 8}; at most `budget` activations in all."""
     rng = np.random.default_rng(seed)
     out, total = [], 0
-    while len(out) < n:
+    for _ in range(1_000_000):
+        if len(out) == n:
+            break
         act = str(rng.choice(["silu", "silu", "swiglu"]))
         mode = "mx" if act == "swiglu" else str(rng.choice(["mx", "b128"]))
         g = 32 if mode == "mx" else 128
@@ -387,6 +393,8 @@ def _random_act_configs(n, seed, budget=1.0e8):
         out.append(dict(act=act, mode=mode, I=I, M=M, std=float(rng.choice([1.0, 2.0, 3.0, 8.0])),
                         copy=bool(rng.random() < 0.5), qin=2 if mode == "mx" and rng.random() < 0.3 else 0,
                         seed=int(rng.integers(1 << 30))))
+    if len(out) < n:
+        raise RuntimeError(f"{n} configurations do not fit a budget of {budget:g} activations")
     return out
 
 
@@ -434,7 +442,9 @@ def _random_quant_configs(n, seed, budget=1.0e8):
     elements in all."""
     rng = np.random.default_rng(seed)
     out, total = [], 0
-    while len(out) < n:
+    for _ in range(1_000_000):
+        if len(out) == n:
+            break
         mode = str(rng.choice(["mx", "b128", "pt"]))
         g = {"mx": 32, "b128": 128, "pt": 8}[mode]
         cols = g * max(1, int(np.exp(rng.uniform(0.0, np.log(32768 // g)))))
@@ -444,6 +454,8 @@ def _random_quant_configs(n, seed, budget=1.0e8):
         total += M * cols
         out.append(dict(mode=mode, dtype=str(rng.choice(["bf16", "fp16", "fp32"])), cols=cols, M=M,
                         seed=int(rng.integers(1 << 30))))
+    if len(out) < n:
+        raise RuntimeError(f"{n} configurations do not fit a budget of {budget:g} elements")
     return out
 
 
